@@ -1,0 +1,159 @@
+/*
+ * csa_index.h -- C ABI of the MI355X (gfx950) CSA lightning-indexer top-k.
+ *
+ * Operation (StreamIndex: Memory-Bounded Compressed Sparse Attention via
+ * Streaming Top-k, Abstract): a lightning indexer scores the compressed keys
+ * for every query position and the top-k keys are selected per query, without
+ * ever materialising the [B, S, H_I, T] score tensor.  For query position t
+ * (batch entry b) and compressed key s the score is
+ *
+ *     I(t, s) = sum_{j < H} w[b,t,j] * max(0, q[b,t,j,:] . k_cmp[b,s,:])
+ *
+ * and key s is visible to t iff (s+1)*m - 1 <= t, i.e. s < min(T, (t+1)/m).
+ * For every t the library returns the min(k, n_vis) visible keys with the
+ * largest scores, ordered by (score descending, key index ascending) -- ties
+ * go to the lower key index -- followed by padding (index -1, score -inf).
+ *
+ * fp8 inputs (OCP E4M3, "fn" finite-only encoding; FP8 Formats for Deep
+ * Learning) carry one positive fp32 scale per row: the dequantised operands
+ * are q_scale[b,t,j] * q[b,t,j,:] and k_scale[b,s] * k_cmp[b,s,:].
+ *
+ * Arithmetic: products of bf16 / e4m3 operands are accumulated in fp32 by
+ * the matrix cores; ReLU, the head weights and the head sum are applied in
+ * fp32.  Integer-valued inputs whose partial sums stay below 2^24 are exact.
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are hipMalloc'd (or torch-allocated) device memory of
+ *     the current device; the caller owns all of them.  The library keeps no
+ *     pointer after a call returns and has no mutable global state.
+ *   - All tensors are dense row-major (C order), innermost dimension last.
+ *   - Calls are asynchronous on `stream`: inputs must stay alive, and outputs
+ *     must not be read, until the stream reaches the work.
+ *   - Every argument is validated before anything is launched; on any error
+ *     nothing is written and a negative csa_status is returned.  No C++
+ *     exception crosses this boundary.
+ *   - Results are deterministic: bitwise identical across runs, chunk sizes
+ *     and launch shapes (no floating-point atomics).
+ */
+#ifndef CSA_INDEX_H
+#define CSA_INDEX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CSA_OK = 0,
+    CSA_ERR_INVALID_ARG = -1,  /* null pointer, bad size, k < 1, m < 1 ... */
+    CSA_ERR_UNSUPPORTED = -2,  /* (dtype, H, D) combination not built       */
+    CSA_ERR_WORKSPACE = -3,    /* caller workspace smaller than required     */
+    CSA_ERR_HIP = -4           /* a HIP runtime call or a launch failed      */
+} csa_status;
+
+typedef enum {
+    CSA_BF16 = 0,          /* q and k_cmp are bfloat16; no scales          */
+    CSA_FP8_E4M3FN = 1     /* q and k_cmp are OCP e4m3fn with fp32 scales  */
+} csa_dtype;
+
+/*
+ * Shapes and dtype of one call.
+ *   q       [B, S, H, D]  dtype      (device)
+ *   w       [B, S, H]     fp32       (device)
+ *   k_cmp   [B, T, D]     dtype      (device)
+ *   q_scale [B, S, H]     fp32 > 0   (device; fp8 only, NULL for bf16)
+ *   k_scale [B, T]        fp32 > 0   (device; fp8 only, NULL for bf16)
+ * Supported: H in {1, 2, 4, 8, 16, 32, 64}; D in {32, 64, 128} for bf16 and
+ * {64, 128} for fp8; B >= 1, S >= 0, T >= 0.  Other combinations return
+ * CSA_ERR_UNSUPPORTED.
+ */
+typedef struct {
+    int64_t B;
+    int64_t S;
+    int64_t T;
+    int32_t H;
+    int32_t D;
+    int32_t dtype;          /* csa_dtype */
+    int32_t reserved0;      /* must be 0 */
+    const float *q_scale;
+    const float *k_scale;
+} csa_desc;
+
+/*
+ * Optional controls (NULL = all defaults).
+ *   chunk_keys   Number of candidate keys a query may buffer beyond its
+ *                running top-k before they are merged into it (the
+ *                partition size of the partition-merge top-k; rounded up to a
+ *                multiple of 64).  0 = default.  Affects speed and workspace
+ *                only, never the result.
+ *   row_offset   Absolute position of q row 0: q row i is position
+ *                row_offset + i (a shard of a longer sequence, or a decode
+ *                step).  Must be >= 0.
+ *   num_cus      Compute units to plan for; 0 = ask the current device.
+ *   workspace    Device scratch of workspace_bytes bytes (256-byte aligned);
+ *                NULL = the library allocates it stream-ordered
+ *                (hipMallocAsync / hipFreeAsync on `stream`).
+ *   timing       Optional pair of hipEvent_t recorded on `stream` right before
+ *                and right after the scoring kernel (for measurements).
+ */
+typedef struct {
+    int32_t chunk_keys;
+    int32_t num_cus;
+    int64_t row_offset;
+    void *workspace;
+    size_t workspace_bytes;
+    hipEvent_t timing[2];
+} csa_options;
+
+/* What a call will do; filled by csa_plan_query (host only, no device work). */
+typedef struct {
+    int32_t queries_per_block;   /* query positions per workgroup block     */
+    int32_t keys_per_tile;       /* compressed keys per staged key tile     */
+    int32_t chunk_keys;          /* effective partition (candidate) size   */
+    int32_t log_capacity;        /* per-query candidate buffer (entries)    */
+    int32_t grid;                /* workgroups of the scoring kernel        */
+    int32_t reserved0;
+    int64_t n_blocks;            /* query blocks over all batch entries     */
+    size_t workspace_bytes;      /* device scratch needed                   */
+} csa_plan_info;
+
+/*
+ * csa_index: top-k compressed keys for every query position.
+ *   out_idx   [B, S, k] int32 (device): key indices, -1 = padding.
+ *   out_score [B, S, k] fp32  (device): scores, -inf = padding.
+ * Both outputs are required.  Uses default options (library-allocated
+ * workspace).  Returns CSA_OK or a negative csa_status.
+ */
+int csa_index(const void *q, const float *w, const void *k_cmp,
+              const csa_desc *desc, int32_t m, int32_t k,
+              int32_t *out_idx, float *out_score, hipStream_t stream);
+
+/* csa_index with explicit options (see csa_options). */
+int csa_index_ex(const void *q, const float *w, const void *k_cmp,
+                 const csa_desc *desc, int32_t m, int32_t k,
+                 int32_t *out_idx, float *out_score,
+                 const csa_options *opt, hipStream_t stream);
+
+/* Device scratch bytes csa_index_ex needs for these arguments (0 on invalid
+ * arguments).  Independent of S and T: it scales with the number of resident
+ * queries and with k + chunk_keys only. */
+size_t csa_workspace_bytes(const csa_desc *desc, int32_t m, int32_t k,
+                           const csa_options *opt);
+
+/* Host-only planning: validates the arguments and reports the launch plan.
+ * Makes no HIP call when opt->num_cus > 0. */
+int csa_plan_query(const csa_desc *desc, int32_t m, int32_t k,
+                   const csa_options *opt, csa_plan_info *out);
+
+/* Static, human-readable text for a csa_status value. */
+const char *csa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA_INDEX_H */

@@ -1,0 +1,14 @@
+"""MI355X-native CSA lightning-indexer top-k (streaming partition-merge).
+
+The compute lives in libcsa_index.so (hand-written gfx950 HIP kernels behind
+the C ABI in include/csa_index.h); this package is its Python binding.
+Importing it loads nothing; the library is loaded on first use and calls
+fail loudly if it is missing.
+"""
+from .binding import (CSA_BF16, CSA_FP8_E4M3FN, CsaError, HipEvents, index, load_library,
+                      make_desc, make_options, plan_query, status_string, workspace_bytes,
+                      workspace_for)
+
+__all__ = ["index", "plan_query", "workspace_bytes", "workspace_for", "load_library",
+           "status_string", "make_desc", "make_options", "CsaError", "HipEvents",
+           "CSA_BF16", "CSA_FP8_E4M3FN"]

@@ -1,0 +1,153 @@
+// csa_abi.cpp -- the extern "C" entry points declared in csa_index.h.
+//
+// Every call validates and plans on the host first (nothing touches the
+// device on an invalid call), then enqueues, on the caller's stream: the
+// scoring kernel (scores + running top-k per query position) and the row
+// sort.  No host synchronisation, no host<->device copies.
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+
+#include "csa_index.h"
+#include "csa_kernels.hpp"
+#include "csa_plan.hpp"
+
+namespace {
+
+int device_cus(int *out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return CSA_ERR_HIP;
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return CSA_ERR_HIP;
+    if (n <= 0) return CSA_ERR_HIP;
+    *out = n;
+    return CSA_OK;
+}
+
+int plan_for(const csa_desc *desc, int32_t m, int32_t k, const csa_options *opt,
+             csa::Plan *p, int *cus)
+{
+    int num_cus = (opt && opt->num_cus > 0) ? opt->num_cus : 0;
+    if (opt && opt->num_cus < 0) return CSA_ERR_INVALID_ARG;
+    // validate everything that does not need the device before asking it
+    const int pre = csa::make_plan(desc, m, k, opt, num_cus > 0 ? num_cus : 1, p);
+    if (pre != CSA_OK) return pre;
+    if (num_cus == 0) {
+        const int rc = device_cus(&num_cus);
+        if (rc != CSA_OK) return rc;
+    }
+    *cus = num_cus;
+    return csa::make_plan(desc, m, k, opt, num_cus, p);
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+}  // namespace
+
+extern "C" const char *csa_status_string(int status)
+{
+    switch (status) {
+    case CSA_OK: return "ok";
+    case CSA_ERR_INVALID_ARG: return "invalid argument";
+    case CSA_ERR_UNSUPPORTED: return "unsupported dtype / head count / head dimension / k";
+    case CSA_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case CSA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+extern "C" int csa_plan_query(const csa_desc *desc, int32_t m, int32_t k,
+                              const csa_options *opt, csa_plan_info *out)
+{
+    if (!out) return CSA_ERR_INVALID_ARG;
+    csa::Plan p;
+    int cus = 0;
+    const int rc = plan_for(desc, m, k, opt, &p, &cus);
+    if (rc != CSA_OK) return rc;
+    out->queries_per_block = p.QB;
+    out->keys_per_tile = csa::kKeysPerTile;
+    out->chunk_keys = p.chunk;
+    out->log_capacity = p.log_cap;
+    out->grid = p.grid;
+    out->reserved0 = 0;
+    out->n_blocks = p.n_blocks;
+    out->workspace_bytes = p.ws_bytes;
+    return CSA_OK;
+}
+
+extern "C" size_t csa_workspace_bytes(const csa_desc *desc, int32_t m, int32_t k,
+                                      const csa_options *opt)
+{
+    csa::Plan p;
+    int cus = 0;
+    if (plan_for(desc, m, k, opt, &p, &cus) != CSA_OK) return 0;
+    return p.ws_bytes;
+}
+
+extern "C" int csa_index_ex(const void *q, const float *w, const void *k_cmp,
+                            const csa_desc *desc, int32_t m, int32_t k,
+                            int32_t *out_idx, float *out_score,
+                            const csa_options *opt, hipStream_t stream)
+{
+    csa::Plan p;
+    int cus = 0;
+    int rc = plan_for(desc, m, k, opt, &p, &cus);
+    if (rc != CSA_OK) return rc;
+    const bool rows = p.B * p.S > 0;
+    if (rows && (!q || !w || !out_idx || !out_score)) return CSA_ERR_INVALID_ARG;
+    if (p.T > 0 && !k_cmp) return CSA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k_cmp, 16) || !aligned(w, 4) || !aligned(out_idx, 4) ||
+        !aligned(out_score, 4) || !aligned(desc->q_scale, 4) || !aligned(desc->k_scale, 4))
+        return CSA_ERR_INVALID_ARG;
+    if (!rows) return CSA_OK;
+
+    void *ws = nullptr;
+    bool owned = false;
+    if (opt && opt->workspace) {
+        if (opt->workspace_bytes < p.ws_bytes || !aligned(opt->workspace, 256))
+            return CSA_ERR_WORKSPACE;
+        ws = opt->workspace;
+    } else if (p.ws_bytes > 0) {
+        if (hipMallocAsync(&ws, p.ws_bytes, stream) != hipSuccess) return CSA_ERR_HIP;
+        owned = true;
+    }
+
+    csa::StreamArgs a;
+    a.q = static_cast<const unsigned char *>(q);
+    a.w = w;
+    a.k = static_cast<const unsigned char *>(k_cmp);
+    a.q_scale = desc->q_scale;
+    a.k_scale = desc->k_scale;
+    a.out_idx = out_idx;
+    a.out_score = out_score;
+    a.ws = static_cast<uint32_t *>(ws);
+    a.B = p.B;
+    a.S = p.S;
+    a.T = p.T;
+    a.row_offset = p.row_offset;
+    a.m = p.m;
+    a.topk = p.k;
+    a.log_cap = p.log_cap;
+    a.blocks_per_batch = p.blocks_per_batch;
+    a.n_blocks = p.n_blocks;
+
+    rc = CSA_OK;
+    if (opt && opt->timing[0] && hipEventRecord(opt->timing[0], stream) != hipSuccess)
+        rc = CSA_ERR_HIP;
+    if (rc == CSA_OK && csa::launch_stream_topk(p, a, stream) != hipSuccess) rc = CSA_ERR_HIP;
+    if (rc == CSA_OK && opt && opt->timing[1] && hipEventRecord(opt->timing[1], stream) != hipSuccess)
+        rc = CSA_ERR_HIP;
+    if (rc == CSA_OK && csa::launch_sort_rows(p, out_idx, out_score, cus, stream) != hipSuccess)
+        rc = CSA_ERR_HIP;
+    if (owned && hipFreeAsync(ws, stream) != hipSuccess && rc == CSA_OK) rc = CSA_ERR_HIP;
+    return rc;
+}
+
+extern "C" int csa_index(const void *q, const float *w, const void *k_cmp,
+                         const csa_desc *desc, int32_t m, int32_t k,
+                         int32_t *out_idx, float *out_score, hipStream_t stream)
+{
+    return csa_index_ex(q, w, k_cmp, desc, m, k, out_idx, out_score, nullptr, stream);
+}

@@ -1,0 +1,50 @@
+// csa_plan.hpp -- host-side validation and launch planning (no HIP calls).
+//
+// The plan splits the query positions of every batch entry into blocks of
+// QB consecutive positions (one workgroup of 8 waves; each wave owns 64
+// (position, head) rows of q = 64/H positions).  A persistent grid walks the
+// blocks heaviest-first; each wave streams the visible compressed keys of its
+// positions in ascending order, 64 keys per staged tile, and keeps a running
+// top-k per position in a bounded candidate log of k + chunk entries
+// (StreamIndex: Memory-Bounded Compressed Sparse Attention via Streaming
+// Top-k, Abstract: chunked partition-merge top-k that never materialises the
+// full score tensor).  The workspace therefore depends on the grid, k and
+// the chunk size, never on S or T.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "csa_index.h"
+
+namespace csa {
+
+constexpr int kWaves = 8;           // waves per workgroup
+constexpr int kThreads = kWaves * 64;
+constexpr int kRowsPerWave = 64;    // (position, head) rows of q per wave
+constexpr int kKeysPerTile = 64;    // compressed keys per LDS tile
+constexpr int kMaxTopK = 16384;     // row sort holds next_pow2(k) keys in LDS
+constexpr int kMaxChunk = 1 << 20;
+
+struct Plan {
+    int64_t B = 0, S = 0, T = 0, row_offset = 0;
+    int H = 0, D = 0, fp8 = 0, m = 0, k = 0;
+    int QW = 0;                 // positions per wave (64 / H)
+    int QB = 0;                 // positions per block (8 * QW)
+    int64_t blocks_per_batch = 0;
+    int64_t n_blocks = 0;
+    int grid = 0;               // scoring workgroups (persistent)
+    int chunk = 0;              // candidates buffered beyond k before a merge
+    int log_cap = 0;            // k + chunk
+    int sort_pow2 = 0;          // next power of two >= k
+    size_t ws_bytes = 0;        // 256-aligned
+};
+
+bool supported(int dtype, int H, int D);
+
+// Validates every argument and fills `plan`.  num_cus must be > 0.
+// Returns CSA_OK or a negative csa_status; never throws.
+int make_plan(const csa_desc *desc, int32_t m, int32_t k,
+              const csa_options *opt, int num_cus, Plan *plan);
+
+}  // namespace csa
