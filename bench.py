@@ -1,0 +1,215 @@
+"""Benchmark of the CSA lightning-indexer top-k on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload s256k] [--no-cpu-baseline]
+
+A step is one csa_index call over the whole workload: scoring of every
+causally visible (query, compressed key) pair on the matrix cores, the
+streaming top-k merge, and the row sort.  Inputs are synthetic, seeded and
+already resident in HBM when the timed region starts.  Prints one JSON line.
+
+value       whole-job indexer queries/s = B*S*K / wall time of K steps
+roofline    the scoring kernel against the bf16 (or fp8) dense MFMA peak:
+            algorithmic flops per launch (2*H*D per visible pair) over the
+            kernel's average duration, from HIP events recorded on the
+            stream it runs on; `traffic` is the HBM bytes per launch from
+            the committed rocprofv3 counter summary when that summary was
+            taken on the current kernel source, else null
+cpu_baseline the CPU oracle (plain C, fp64) on a seeded sample of rows of
+            the same workload, on this host's cores
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "indexer queries/sec + MFMA TFLOP/s (% peak) + peak HBM GB at S=262K, 1 GPU"
+PEAK_TFLOPS = {"bf16": 2500.0, "e4m3fn": 5000.0}   # MI355X dense MFMA
+KERNEL_SRC = os.path.join(ROOT, "streaming_top_selection_csa_amd", "csrc", "csa_kernels.hip")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "stream_topk_s256k_pmc.md")
+
+
+def visible_pairs(S, T, m, B=1, row_offset=0):
+    """Number of (query, key) pairs with key s visible to position t, i.e.
+    sum over t in [row_offset, row_offset+S) of min(T, (t+1)//m), in closed
+    form: with G(x) = sum_{u=0}^{x} min(T, u//m) the answer is
+    G(row_offset+S) - G(row_offset)."""
+    def G(x):
+        full = m * T - 1            # u >= m*T sees all T keys
+        y = min(x, full)
+        q, r = divmod(y, m)         # sum_{u=0}^{y} u//m
+        tot = m * q * (q - 1) // 2 + q * (r + 1)
+        if x > full:
+            tot += (x - full) * T
+        return tot
+    if S <= 0:
+        return 0
+    return B * (G(row_offset + S) - G(row_offset))
+
+
+def kernel_sha():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_from_profile(workload):
+    """HBM bytes per scoring launch from the committed counter summary, if it
+    was taken on this kernel source and workload."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    text = open(PMC_SUMMARY).read()
+    sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    wl = re.search(r"workload:\s*(\S+)", text)
+    tb = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (sha and wl and tb) or sha.group(1) != kernel_sha() or wl.group(1) != workload:
+        return None
+    return float(tb.group(1))
+
+
+def cpu_baseline(inp, wl, nrows, seed=0):
+    import numpy as np
+
+    import oracle
+    from csa_synth import storage_numpy
+
+    rng = np.random.default_rng(seed)
+    rows = np.sort(rng.choice(wl.S, size=min(nrows, wl.S), replace=False)).astype(np.int64)
+    rt = __import__("torch").as_tensor(rows, device=inp["q"].device)
+    q = storage_numpy(inp["q"][0].index_select(0, rt))
+    w = inp["w"][0].index_select(0, rt).cpu().numpy()
+    k = storage_numpy(inp["k"][0])
+    qs = inp["q_scale"][0].index_select(0, rt).cpu().numpy() if "q_scale" in inp else None
+    ks = inp["k_scale"][0].cpu().numpy() if "k_scale" in inp else None
+    threads = min(len(rows), int(os.environ.get("OMP_NUM_THREADS", "0")) or (os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    oracle.topk_rows(q, w, k, rows, wl.m, wl.k, dtype=wl.dtype, q_scale_rows=qs, k_scale=ks,
+                     nthreads=threads)
+    dt = time.perf_counter() - t0
+    n_vis = np.minimum(wl.n_keys, (rows + 1) // wl.m)
+    return {"value": len(rows) / dt, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": (f"{len(rows)} seeded uniform rows of {wl.name} (mean visible keys "
+                       f"{float(n_vis.mean()):.0f}; workload mean {wl.n_keys / 2:.0f}), "
+                       f"fp64 scores + full sort, {dt:.1f} s")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="s256k")
+    ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (5 times), to scale "
+                         "the HBM byte counters of a profiler run")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build measures one GPU only (the indexer path is single-GPU); "
+              "run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import streaming_top_selection_csa_amd as csa
+    from csa_synth import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 5}))
+        return
+    csa.load_library()
+    wl = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    inp = make_inputs(wl, seed=0, device=dev)
+    out_idx = torch.empty((wl.B, wl.S, wl.k), dtype=torch.int32, device=dev)
+    out_score = torch.empty((wl.B, wl.S, wl.k), dtype=torch.float32, device=dev)
+    ws = csa.workspace_for(inp["q"], inp["k"], wl.m, wl.k, args.chunk)
+    torch.cuda.synchronize()
+    in_bytes = sum(t.numel() * t.element_size() for t in inp.values())
+    out_bytes = out_idx.numel() * 4 + out_score.numel() * 4
+    ws_bytes = ws.numel()
+    events = csa.HipEvents(args.steps)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(timing=None):
+        csa.index(inp["q"], inp["w"], inp["k"], wl.m, wl.k, q_scale=inp.get("q_scale"),
+                  k_scale=inp.get("k_scale"), out_idx=out_idx, out_score=out_score,
+                  chunk_keys=args.chunk, workspace=ws, timing=timing, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events.pairs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kernel_ms = [events.elapsed_ms(i) for i in range(args.steps)]
+    events.close()
+    peak_hbm = torch.cuda.max_memory_allocated(dev)
+
+    pairs = visible_pairs(wl.S, wl.n_keys, wl.m, wl.B)
+    flops = 2.0 * wl.H * wl.D * pairs
+    ms_per_step = 1e3 * elapsed / args.steps
+    kernel_avg = sum(kernel_ms) / len(kernel_ms)
+    peak = PEAK_TFLOPS[wl.dtype]
+    achieved = flops / (kernel_avg * 1e-3) / 1e12
+    step_tflops = flops / (ms_per_step * 1e-3) / 1e12
+    qps = wl.B * wl.S * args.steps / elapsed
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, wl, args.cpu_rows)
+
+    line = {
+        "metric": METRIC,
+        "value": qps,
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype if wl.dtype != "e4m3fn" else "fp8-e4m3",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "S": wl.S, "T": wl.n_keys, "H_I": wl.H,
+                   "d_I": wl.D, "m": wl.m, "k": wl.k, "dist": wl.dist,
+                   "chunk_keys": args.chunk or None},
+        "tflops": step_tflops,
+        "mfma_pct_peak": 100.0 * step_tflops / peak,
+        "peak_hbm_gb": peak_hbm / 1e9,
+        "hbm_breakdown_gb": {"inputs": in_bytes / 1e9, "outputs": out_bytes / 1e9,
+                             "workspace": ws_bytes / 1e9},
+        "scoring_kernel_ms": kernel_avg,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": traffic_from_profile(wl.name)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

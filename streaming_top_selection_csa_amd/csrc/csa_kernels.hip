@@ -48,6 +48,14 @@ __device__ __forceinline__ float key_to_float(uint32_t u)
     return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
 }
 
+// max(x, 0) for finite x as one signed-integer max on the bit pattern:
+// negative floats (and -0) have the sign bit set, i.e. are negative ints.
+__device__ __forceinline__ float relu(float x)
+{
+    const int b = __float_as_int(x);
+    return __int_as_float(b > 0 ? b : 0);
+}
+
 // Number of set bits of `m` in lanes below this lane.
 __device__ __forceinline__ int lanes_below(uint64_t m)
 {
@@ -75,6 +83,28 @@ __device__ __forceinline__ void wave_global_sync()
 {
     __threadfence();
     __builtin_amdgcn_wave_barrier();
+}
+
+// Inclusive prefix sum over the 64 lanes (lane 0 first), on DPP row shifts
+// and row broadcasts (no LDS round trips).
+__device__ __forceinline__ uint32_t wave_prefix_sum(uint32_t v)
+{
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return v;
+}
+
+// For lane l < 32 returns x[l] + x[l+32]; for lane l >= 32 returns
+// y[l-32] + y[l] (one v_permlane32_swap exchanges the crossing halves).
+__device__ __forceinline__ float cross_half_sum(float x, float y)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // MFMA operand traits: bf16 32x32x16 (8 bf16 per lane) or fp8 e4m3
@@ -124,27 +154,40 @@ struct Op<true> {
 
 // ------------------------------------------------------- candidate merging
 
+constexpr int kBatch = 8;  // log entries per lane in flight in the log passes
+
 // The log lu/li[0..n) holds candidates of one position in ascending key
 // order, n > k.  Finds the k-th best under (score desc, key asc) with a
 // 4 x 8-bit radix select on the order keys, compacts the log in place to
 // exactly the k best (still in key order) and returns the k-th best key.
+// rhist: 256 words of LDS private to the wave.
 __device__ __noinline__ uint32_t merge_log(uint32_t *lu, int32_t *li, int n, int k,
-                                           uint32_t *hist, int lane)
+                                           uint32_t *rhist, int lane)
 {
     wave_global_sync();
     uint32_t prefix = 0u, pmask = 0u;
     int kk = k;  // rank, from the top, of the wanted key among prefix matches
 #pragma unroll 1
     for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int i = lane; i < 256; i += 64) hist[i] = 0u;
+        for (int i = lane; i < 256; i += 64) rhist[i] = 0u;
         wave_lds_sync();
-        for (int e = lane; e < n; e += 64) {
-            const uint32_t u = lu[e];
-            if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+#pragma unroll 1
+        for (int base = 0; base < n; base += 64 * kBatch) {
+            uint32_t u[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const int e = base + 64 * j + lane;
+                u[j] = e < n ? lu[e] : 0u;
+            }
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const int e = base + 64 * j + lane;
+                if (e < n && (u[j] & pmask) == prefix) atomicAdd(&rhist[(u[j] >> shift) & 255u], 1u);
+            }
         }
         wave_lds_sync();
-        const uint32_t c0 = hist[4 * lane], c1 = hist[4 * lane + 1];
-        const uint32_t c2 = hist[4 * lane + 2], c3 = hist[4 * lane + 3];
+        const uint32_t c0 = rhist[4 * lane], c1 = rhist[4 * lane + 1];
+        const uint32_t c2 = rhist[4 * lane + 2], c3 = rhist[4 * lane + 3];
         const uint32_t cl = c0 + c1 + c2 + c3;
         uint32_t sfx = cl;  // count in digits >= 4*lane
 #pragma unroll
@@ -182,107 +225,266 @@ __device__ __noinline__ uint32_t merge_log(uint32_t *lu, int32_t *li, int n, int
     // equal ones (the lowest key indices, since the log is in key order).
     int wpos = 0, eq_seen = 0;
 #pragma unroll 1
-    for (int base = 0; base < n; base += 64) {
-        const int e = base + lane;
-        const bool valid = e < n;
-        const uint32_t u = valid ? lu[e] : 0u;
-        const int32_t id = valid ? li[e] : 0;
-        const bool gt = valid && u > prefix;
-        const bool eq = valid && u == prefix;
-        const uint64_t meq = __ballot(eq);
-        const bool keep = gt || (eq && eq_seen + lanes_below(meq) < kk);
-        const uint64_t mk = __ballot(keep);
-        if (keep) {
-            const int p = wpos + lanes_below(mk);
-            lu[p] = u;
-            li[p] = id;
+    for (int base = 0; base < n; base += 64 * kBatch) {
+        uint32_t u[kBatch];
+        int32_t id[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const int e = base + 64 * j + lane;
+            u[j] = e < n ? lu[e] : 0u;
+            id[j] = e < n ? li[e] : 0;
         }
-        wpos += __popcll(mk);
-        eq_seen += __popcll(meq);
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const bool valid = base + 64 * j + lane < n;
+            const bool gt = valid && u[j] > prefix;
+            const bool eq = valid && u[j] == prefix;
+            const uint64_t meq = __ballot(eq);
+            const bool keep = gt || (eq && eq_seen + lanes_below(meq) < kk);
+            const uint64_t mk = __ballot(keep);
+            if (keep) {
+                const int p = wpos + lanes_below(mk);
+                lu[p] = u[j];
+                li[p] = id[j];
+            }
+            wpos += __popcll(mk);
+            eq_seen += __popcll(meq);
+        }
     }
     wave_global_sync();
     return prefix;
 }
 
+// Drops, in place and in order, every log entry whose key is below tau
+// (such an entry is beaten by at least k earlier ones); returns the count.
+__device__ __noinline__ int compact_log(uint32_t *lu, int32_t *li, int n, uint32_t tau, int lane)
+{
+    wave_global_sync();
+    int wpos = 0;
+#pragma unroll 1
+    for (int base = 0; base < n; base += 64 * kBatch) {
+        uint32_t u[kBatch];
+        int32_t id[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const int e = base + 64 * j + lane;
+            u[j] = e < n ? lu[e] : 0u;
+            id[j] = e < n ? li[e] : 0;
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const bool keep = base + 64 * j + lane < n && u[j] >= tau;
+            const uint64_t mk = __ballot(keep);
+            if (keep) {
+                const int p = wpos + lanes_below(mk);
+                lu[p] = u[j];
+                li[p] = id[j];
+            }
+            wpos += __popcll(mk);
+        }
+    }
+    wave_global_sync();
+    return wpos;
+}
+
+// ---------------------------------------------------- threshold histogram
+//
+// Each position keeps, in LDS, counts of its live candidates over NB bins
+// of the order key u: bin = (u >> 16) - base, i.e. 128 bins per binade of
+// |score| (sign, 8 exponent bits, 7 mantissa bits), clamped to bin 0 below
+// the window.  If the bins at and above b hold at least k candidates, every
+// later key whose u is below the lower edge of bin b is beaten by k earlier
+// ones, so the filter threshold may rise to that edge minus one without
+// reading the log; bins below b are then dead and are cleared.
+
+template <int NB>
+struct Hist {
+    static constexpr int PER = NB >= 64 ? NB / 64 : 1;  // bins per lane
+
+    static __device__ __forceinline__ void clear(uint32_t *h, int lane)
+    {
+#pragma unroll
+        for (int j = 0; j < PER; ++j)
+            if (lane * PER + j < NB) h[lane * PER + j] = 0u;
+    }
+
+    // Highest bin b with at least `need` counts in bins >= b, or -1.
+    // Lane l owns the PER bins just below NB - l*PER (lane 0 the top ones),
+    // so a prefix sum over lanes counts everything at or above a lane's bins.
+    static __device__ __forceinline__ int top_bin(const uint32_t *h, int need, int lane)
+    {
+        uint32_t c[PER];
+        uint32_t cl = 0u;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int b = NB - 1 - (lane * PER + j);
+            c[j] = b >= 0 ? h[b] : 0u;
+            cl += c[j];
+        }
+        const uint32_t pre = wave_prefix_sum(cl);
+        const uint64_t bal = __ballot(pre >= uint32_t(need));
+        if (bal == 0) return -1;
+        const int L = __ffsll(static_cast<unsigned long long>(bal)) - 1;
+        uint32_t acc = pre - cl;
+        int b = NB - 1 - (lane * PER + PER - 1);
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            acc += c[j];
+            if (acc >= uint32_t(need)) {
+                b = NB - 1 - (lane * PER + j);
+                break;
+            }
+        }
+        return __shfl(b, L);
+    }
+
+    static __device__ __forceinline__ void zero_below(uint32_t *h, int b, int lane)
+    {
+#pragma unroll
+        for (int j = 0; j < PER; ++j)
+            if (lane * PER + j < b && lane * PER + j < NB) h[lane * PER + j] = 0u;
+    }
+
+    // Moves the window up by delta > 0 bins; counts falling below it are
+    // clamped into bin 0.
+    static __device__ __forceinline__ void shift(uint32_t *h, int delta, int lane)
+    {
+        uint32_t c[PER];
+#pragma unroll
+        for (int j = 0; j < PER; ++j) c[j] = lane * PER + j < NB ? h[lane * PER + j] : 0u;
+        wave_lds_sync();
+        clear(h, lane);
+        wave_lds_sync();
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int nb = lane * PER + j - delta;
+            if (c[j]) atomicAdd(&h[nb > 0 ? nb : 0], c[j]);
+        }
+        wave_lds_sync();
+    }
+};
+
+__device__ __forceinline__ int wave_max(int v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const int o = __shfl_xor(v, off);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+// Re-counts the k log entries left by an exact merge (window unchanged).
+template <int NB>
+__device__ __noinline__ void hist_recount(uint32_t *h, int hbase, const uint32_t *lu, int n, int lane)
+{
+    wave_global_sync();
+    Hist<NB>::clear(h, lane);
+    wave_lds_sync();
+#pragma unroll 1
+    for (int base = 0; base < n; base += 64 * kBatch) {
+        uint32_t u[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const int e = base + 64 * j + lane;
+            u[j] = e < n ? lu[e] : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            if (base + 64 * j + lane < n) {
+                const int lb = int(u[j] >> 16) - hbase;
+                atomicAdd(&h[lb > 0 ? (lb < NB ? lb : NB - 1) : 0], 1u);
+            }
+        }
+    }
+    wave_lds_sync();
+}
+
 // ------------------------------------------------------------ score epilogue
 
-// acc[hb][ks][i] is the dot product of q row R = hb*32 + 8*(i/4) +
-// 4*half + i%4 (of the wave's 64 (position, head) rows) with key
-// ks*32 + lane%32 of the tile.  wr[hb][i] is the head weight of row R.
-// On return sc[qi] holds, in lane l, the score of the wave's position qi
-// against key l of the tile: sum over the position's heads of w*ReLU(dot).
+// After the MFMAs of one 32-key half of a tile, acc[hb][i] is the dot
+// product of q row R = hb*32 + 8*(i/4) + 4*half + i%4 (of the wave's 64
+// (position, head) rows) with key lane%32 of that half, and wr[hb][i] is the
+// head weight of row R.  partial() folds ReLU, the weights and the part of
+// the head sum a lane can do alone; combine() joins the two halves of the
+// tile so that sc[qi] holds, in lane l, the score of the wave's position qi
+// against key l of the tile.
 template <int H>
-__device__ __forceinline__ void head_reduce(const f32x16_t (&acc)[2][2], const float (&wr)[2][16],
-                                            float (&sc)[64 / H], int half)
-{
-    constexpr int QW = 64 / H;
-    if constexpr (H >= 8) {
-        // a lane's rows of one 8-row group belong to one position; the other
-        // half-wave holds the remaining heads of the same key column.
-        float s[QW][2];
+struct Epi {
+    static constexpr int QW = 64 / H;
+    // H >= 8: one partial per position; H <= 4: one per (hb, 8-row group,
+    // position inside a 4-row quad) slot, each slot holding a lower-half and
+    // an upper-half position.
+    static constexpr int NP = H >= 8 ? QW : 32 / H;
+
+    static __device__ __forceinline__ void partial(const f32x16_t (&acc)[2], const float (&wr)[2][16],
+                                                   float (&p)[NP])
+    {
 #pragma unroll
-        for (int qi = 0; qi < QW; ++qi) s[qi][0] = s[qi][1] = 0.f;
+        for (int x = 0; x < NP; ++x) p[x] = 0.f;
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int qi = (hb * 32 + 8 * (i >> 2)) / H;
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    s[qi][ks] += wr[hb][i] * fmaxf(acc[hb][ks][i], 0.f);
+                const int x = H >= 8 ? (hb * 32 + 8 * (i >> 2)) / H
+                                     : (hb * 4 + (i >> 2)) * (4 / H) + (i & 3) / H;
+                p[x] += wr[hb][i] * relu(acc[hb][i]);
             }
-#pragma unroll
-        for (int qi = 0; qi < QW; ++qi) {
-            const float give = half ? s[qi][0] : s[qi][1];
-            const float got = __shfl_xor(give, 32);
-            sc[qi] = (half ? s[qi][1] : s[qi][0]) + got;
-        }
-    } else {
-        // H <= 4: each half-wave holds whole positions; pair a lower-half
-        // position with an upper-half one and swap the key halves.
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-#pragma unroll
-                for (int rho = 0; rho < 4 / H; ++rho) {
-                    float val[2] = {0.f, 0.f};
-#pragma unroll
-                    for (int r = H * rho; r < H * rho + H; ++r)
-#pragma unroll
-                        for (int ks = 0; ks < 2; ++ks)
-                            val[ks] += wr[hb][4 * g + r] * fmaxf(acc[hb][ks][4 * g + r], 0.f);
-                    const float give = half ? val[0] : val[1];
-                    const float got = __shfl_xor(give, 32);
-                    const int qlo = (hb * 32 + 8 * g + H * rho) / H;
-                    const int qhi = (hb * 32 + 8 * g + 4 + H * rho) / H;
-                    sc[qlo] = half ? got : val[0];
-                    sc[qhi] = half ? val[1] : got;
-                }
     }
-}
+
+    static __device__ __forceinline__ void combine(const float (&p0)[NP], const float (&p1)[NP],
+                                                   float (&sc)[QW])
+    {
+        if constexpr (H >= 8) {
+            // the other half-wave holds the remaining heads of the same keys
+#pragma unroll
+            for (int qi = 0; qi < QW; ++qi) sc[qi] = cross_half_sum(p0[qi], p1[qi]);
+        } else {
+            // lower lanes hold position qlo, upper lanes qhi, for the keys of
+            // their half-tile; one swap gives each lane both positions at
+            // key l of the tile
+#pragma unroll
+            for (int x = 0; x < NP; ++x) {
+                const int hb = x / (4 * (4 / H));
+                const int g = (x / (4 / H)) % 4;
+                const int rho = x % (4 / H);
+                const int qlo = (hb * 32 + 8 * g + H * rho) / H;
+                const int qhi = (hb * 32 + 8 * g + 4 + H * rho) / H;
+                const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0[x]),
+                                                                __float_as_uint(p1[x]), false, false);
+                sc[qlo] = __uint_as_float(r[0]);
+                sc[qhi] = __uint_as_float(r[1]);
+            }
+        }
+    }
+};
 
 // ------------------------------------------------------------ scoring kernel
 
 template <int H, int D, bool FP8>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 stream_topk_kernel(StreamArgs a)
 {
     using O = Op<FP8>;
     using OpT = typename O::T;
-    constexpr int QW = kRowsPerWave / H;             // positions per wave
+    using E = Epi<H>;
+    constexpr int QW = 64 / H;                       // positions per wave (64 rows)
     constexpr int QB = kWaves * QW;                  // positions per block
     constexpr int KT = kKeysPerTile;
-    constexpr int NDS = D / O::KSTEP;                // K steps per tile
+    constexpr int NDS = D / O::KSTEP;                // K steps per half tile
     constexpr int ROWB = D * O::ESZ + 16;            // padded LDS key row
     constexpr int TILEB = KT * ROWB;
     constexpr int RV = D * O::ESZ / 16;              // 16-byte vectors per key row
     constexpr int NV = KT * RV;                      // vectors per tile
     constexpr int VPT = (NV + kThreads - 1) / kThreads;
+    constexpr int NB = 512 / QW;                     // threshold bins per position
+    constexpr int HEAD = NB / 8 > 1 ? NB / 8 : 1;    // headroom above the max seen
+    constexpr int UPD = 64;                          // appends between refreshes
 
     __shared__ __attribute__((aligned(16))) unsigned char s_k[2][TILEB];
     __shared__ float s_ks[2][KT];
-    __shared__ uint32_t s_hist[kWaves][256];
+    __shared__ uint32_t s_rhist[kWaves][256];       // radix select scratch
+    __shared__ uint32_t s_th[kWaves][QW * NB];      // threshold histograms
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -294,12 +496,18 @@ stream_topk_kernel(StreamArgs a)
     const int64_t slot = int64_t(g) * kWaves + wave;
     uint32_t *const log_u = a.ws + slot * (2 * int64_t(QW) * a.log_cap);
     int32_t *const log_i = reinterpret_cast<int32_t *>(log_u + int64_t(QW) * a.log_cap);
-    uint32_t *const hist = s_hist[wave];
+    uint32_t *const rhist = s_rhist[wave];
 
-    // heaviest blocks first (late positions see the most keys); snake order
-    // over the persistent grid evens out the per-workgroup totals.
+    // Heaviest blocks first (late positions see the most keys), snake order
+    // over the persistent grid to even out the per-workgroup totals.  With
+    // a multiple of 8 workgroups, workgroup g runs on XCD g % 8; the blocks
+    // of one round are then dealt so that each XCD's workgroups hold
+    // consecutive blocks, which stream the same key tiles through that
+    // XCD's L2 at about the same time.
+    const int xcd = g & 7, in_xcd = g >> 3, per_xcd = G >> 3;
     for (int64_t rnd = 0;; ++rnd) {
-        const int64_t j = rnd * G + ((rnd & 1) ? (G - 1 - g) : g);
+        const int64_t j = (G & 7) ? rnd * G + ((rnd & 1) ? (G - 1 - g) : g)
+                                  : (rnd * 8 + ((rnd & 1) ? 7 - xcd : xcd)) * per_xcd + in_xcd;
         if (j >= a.n_blocks) break;
         const int64_t b = j % a.B;
         const int64_t blk = a.blocks_per_batch - 1 - j / a.B;
@@ -332,19 +540,85 @@ stream_topk_kernel(StreamArgs a)
             }
         }
         int nv[QW];
-        uint32_t tau[QW];
-        int cnt[QW];
-        int nv_max = 0;
+        uint32_t tau[QW];   // a later key at or below tau is beaten by k earlier keys
+        int cnt[QW];        // log entries
+        int pend[QW];       // appends since the last threshold refresh
+        int hbase[QW];      // global bin of threshold-histogram bin 0
 #pragma unroll
         for (int qi = 0; qi < QW; ++qi) {
             const int64_t pos = wp0 + qi;
             nv[qi] = pos < a.S ? int(n_visible(a.row_offset + pos, a.T, a.m)) : 0;
             tau[qi] = 0u;  // below the key of any finite score: accept all
             cnt[qi] = 0;
-            nv_max = nv[qi] > nv_max ? nv[qi] : nv_max;
+            pend[qi] = 0;
+            hbase[qi] = 0;
+            Hist<NB>::clear(&s_th[wave][qi * NB], lane);
         }
+        wave_lds_sync();
 
-        // ---- key tiles: global -> registers -> LDS, double buffered
+        // Filter the wave's scores against key tile `it` and append the
+        // survivors to the candidate logs (see the threshold histogram).
+        auto consume = [&](const float (&sc)[QW], int it) {
+            const int kt = it * KT;
+            const int key = kt + lane;
+#pragma unroll
+            for (int qi = 0; qi < QW; ++qi) {
+                const int r = qi;
+                if (kt >= nv[qi]) continue;  // wave-uniform
+                const uint32_t u = order_key(sc[r]);
+                const bool pass = key < nv[qi] && u > tau[qi];
+                const uint64_t mk = __ballot(pass);
+                if (mk == 0) continue;
+                uint32_t *h = &s_th[wave][qi * NB];
+                const int gb = int(u >> 16);
+                if (cnt[qi] == 0) {
+                    hbase[qi] = wave_max(pass ? gb : -1) + HEAD - (NB - 1);
+                } else if (__ballot(pass && gb > hbase[qi] + NB - 1)) {
+                    const int gmax = wave_max(pass ? gb : -1);
+                    const int delta = gmax + HEAD - (hbase[qi] + NB - 1);
+                    Hist<NB>::shift(h, delta, lane);
+                    hbase[qi] += delta;
+                }
+                uint32_t *lu = log_u + qi * a.log_cap;
+                int32_t *li = log_i + qi * a.log_cap;
+                if (pass) {
+                    const int p = cnt[qi] + lanes_below(mk);
+                    lu[p] = u;
+                    li[p] = key;
+                    const int lb = gb - hbase[qi];
+                    atomicAdd(&h[lb > 0 ? lb : 0], 1u);
+                }
+                const int added = __popcll(mk);
+                cnt[qi] += added;
+                pend[qi] += added;
+                const bool full = cnt[qi] > a.log_cap - KT;
+                if (cnt[qi] >= a.topk && (pend[qi] >= UPD || full)) {
+                    // raise tau to the lower edge of the highest bin that
+                    // still has k candidates at or above it, minus one
+                    wave_lds_sync();
+                    const int bstar = Hist<NB>::top_bin(h, a.topk, lane);
+                    const int gstar = hbase[qi] + bstar;
+                    if (bstar > 0 && gstar > 0) {
+                        const uint32_t t2 = (uint32_t(gstar) << 16) - 1u;
+                        if (t2 > tau[qi]) tau[qi] = t2;
+                        Hist<NB>::zero_below(h, bstar, lane);
+                    }
+                    pend[qi] = 0;
+                }
+                if (full) {
+                    cnt[qi] = compact_log(lu, li, cnt[qi], tau[qi], lane);
+                    const int room = a.topk + (a.log_cap - a.topk) / 2;
+                    if (cnt[qi] > (room < a.log_cap - KT ? room : a.log_cap - KT)) {
+                        // the bins could not separate enough: exact merge
+                        tau[qi] = merge_log(lu, li, cnt[qi], a.topk, rhist, lane);
+                        cnt[qi] = a.topk;
+                        hist_recount<NB>(h, hbase[qi], lu, cnt[qi], lane);
+                    }
+                }
+            }
+        };
+
+        // ---- key tiles: global -> registers -> LDS (double buffered)
         const unsigned char *kbase = a.k + b * a.T * (D * O::ESZ);
         const float *ksbase = FP8 ? a.k_scale + b * a.T : nullptr;
         u32x4_t pre[VPT];
@@ -376,70 +650,64 @@ stream_topk_kernel(StreamArgs a)
             if constexpr (FP8)
                 if (tid < KT) s_ks[buf][tid] = pks;
         };
+        // the MFMAs of the wave's rows against both 32-key halves of LDS tile buf
+        f32x16_t acc[2][2];
+        auto mma_tile = [&](int buf) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const unsigned char *kb = &s_k[buf][(ks * 32 + col) * ROWB + half * O::LANE_BYTES];
+#pragma unroll
+                for (int ds = 0; ds < NDS; ++ds) {
+                    const OpT bk = O::load(kb + ds * O::KSTEP * O::ESZ);
+#pragma unroll
+                    for (int hb = 0; hb < 2; ++hb)
+                        acc[ks][hb] = O::mma(qa[hb][ds], bk, ds == 0 ? f32x16_t{} : acc[ks][hb]);
+                }
+            }
+        };
+        // epilogue of the accumulated tile it, then the filter and appends
+        auto epilogue = [&](int it, float ksv) {
+            float p0[E::NP], p1[E::NP], sc[QW];
+            E::partial(acc[0], wr, p0);
+            E::partial(acc[1], wr, p1);
+            E::combine(p0, p1, sc);
+            if constexpr (FP8)
+#pragma unroll
+                for (int qi = 0; qi < QW; ++qi) sc[qi] *= ksv;
+            consume(sc, it);
+        };
 
+        // Waves 0-3 score tile i and then run its epilogue; waves 4-7 (the
+        // second wave of each SIMD) first finish the epilogue of tile i-1 and
+        // then score tile i.  The two waves sharing a SIMD are thus half a
+        // period apart: one issues MFMAs while the other runs VALU work.
+        const bool lagging = wave >= kWaves / 2;
         const int ntiles = (n_hi + KT - 1) / KT;
         if (ntiles > 0) {
             load_tile(0);
             store_tile(0);
         }
         __syncthreads();
+        float ksv_prev = 1.f;
 #pragma unroll 1
         for (int it = 0; it < ntiles; ++it) {
             const int buf = it & 1;
             const bool more = it + 1 < ntiles;
             if (more) load_tile(it + 1);
-            const int kt = it * KT;
-            if (kt < nv_max) {
-                f32x16_t acc[2][2];
-#pragma unroll
-                for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-                    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                        for (int e = 0; e < 16; ++e) acc[hb][ks][e] = 0.f;
-                const unsigned char *kb = &s_k[buf][col * ROWB + half * O::LANE_BYTES];
-#pragma unroll
-                for (int ds = 0; ds < NDS; ++ds) {
-                    const OpT b0 = O::load(kb + ds * O::KSTEP * O::ESZ);
-                    const OpT b1 = O::load(kb + 32 * ROWB + ds * O::KSTEP * O::ESZ);
-#pragma unroll
-                    for (int hb = 0; hb < 2; ++hb) {
-                        acc[hb][0] = O::mma(qa[hb][ds], b0, acc[hb][0]);
-                        acc[hb][1] = O::mma(qa[hb][ds], b1, acc[hb][1]);
-                    }
-                }
-                float sc[QW];
-                head_reduce<H>(acc, wr, sc, half);
-                if constexpr (FP8) {
-                    const float ksv = s_ks[buf][lane];
-#pragma unroll
-                    for (int qi = 0; qi < QW; ++qi) sc[qi] *= ksv;
-                }
-                const int key = kt + lane;
-#pragma unroll
-                for (int qi = 0; qi < QW; ++qi) {
-                    if (kt >= nv[qi]) continue;  // wave-uniform
-                    const uint32_t u = order_key(sc[qi]);
-                    const bool pass = key < nv[qi] && u > tau[qi];
-                    const uint64_t mk = __ballot(pass);
-                    if (mk == 0) continue;
-                    uint32_t *lu = log_u + qi * a.log_cap;
-                    int32_t *li = log_i + qi * a.log_cap;
-                    if (pass) {
-                        const int p = cnt[qi] + lanes_below(mk);
-                        lu[p] = u;
-                        li[p] = key;
-                    }
-                    cnt[qi] += __popcll(mk);
-                    if (cnt[qi] > a.log_cap - KT) {
-                        tau[qi] = merge_log(lu, li, cnt[qi], a.topk, hist, lane);
-                        cnt[qi] = a.topk;
-                    }
-                }
+            float ksv = 1.f;
+            if constexpr (FP8) ksv = s_ks[buf][lane];
+            if (!lagging) {
+                mma_tile(buf);
+                epilogue(it, ksv);
+            } else {
+                if (it > 0) epilogue(it - 1, ksv_prev);
+                mma_tile(buf);
             }
+            ksv_prev = ksv;
             if (more) store_tile(buf ^ 1);
             __syncthreads();
         }
+        if (lagging && ntiles > 0) epilogue(ntiles - 1, ksv_prev);
 
         // ---- final merge and (unsorted, key-ordered) output rows
 #pragma unroll 1
@@ -450,7 +718,7 @@ stream_topk_kernel(StreamArgs a)
             int32_t *li = log_i + qi * a.log_cap;
             int c = cnt[qi];
             if (c > a.topk) {
-                merge_log(lu, li, c, a.topk, hist, lane);
+                merge_log(lu, li, c, a.topk, rhist, lane);
                 c = a.topk;
             } else {
                 wave_global_sync();

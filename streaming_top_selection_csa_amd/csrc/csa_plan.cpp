@@ -53,7 +53,10 @@ int make_plan(const csa_desc *desc, int32_t m, int32_t k,
     if (rows > (int64_t(1) << 46) / (int64_t(desc->H) * desc->D)) return CSA_ERR_INVALID_ARG;
     if (rows > (int64_t(1) << 46) / k) return CSA_ERR_INVALID_ARG;
 
-    if (chunk == 0) chunk = k > 1024 ? k : 1024;           // default partition
+    if (chunk == 0) {  // default partition: 4k, within [1024, 8192]
+        const int64_t c = int64_t(4) * k;
+        chunk = int(c < 1024 ? 1024 : (c > 8192 ? 8192 : c));
+    }
     chunk = (chunk + kKeysPerTile - 1) / kKeysPerTile * kKeysPerTile;
 
     Plan p;

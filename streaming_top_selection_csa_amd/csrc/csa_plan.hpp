@@ -19,7 +19,7 @@
 
 namespace csa {
 
-constexpr int kWaves = 8;           // waves per workgroup
+constexpr int kWaves = 8;           // waves per workgroup (two per SIMD)
 constexpr int kThreads = kWaves * 64;
 constexpr int kRowsPerWave = 64;    // (position, head) rows of q per wave
 constexpr int kKeysPerTile = 64;    // compressed keys per LDS tile
