@@ -125,6 +125,11 @@ struct Op<false> {
         return __builtin_bit_cast(T, *reinterpret_cast<const u32x4_t *>(p));
     }
     static __device__ __forceinline__ T zero() { return __builtin_bit_cast(T, u32x4_t{0, 0, 0, 0}); }
+    // operand chunk c of an LDS key row stored with chunk swizzle `swz`
+    static __device__ __forceinline__ T load_swz(const unsigned char *row, int c, int swz)
+    {
+        return load(row + ((c ^ swz) << 4));
+    }
     static __device__ __forceinline__ f32x16_t mma(T a, T b, f32x16_t c)
     {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -145,6 +150,13 @@ struct Op<true> {
                  int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
     }
     static __device__ __forceinline__ T zero() { return T{0, 0, 0, 0, 0, 0, 0, 0}; }
+    static __device__ __forceinline__ T load_swz(const unsigned char *row, int c, int swz)
+    {
+        const u32x4_t lo = *reinterpret_cast<const u32x4_t *>(row + ((c ^ swz) << 4));
+        const u32x4_t hi = *reinterpret_cast<const u32x4_t *>(row + (((c + 1) ^ swz) << 4));
+        return T{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]),
+                 int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+    }
     static __device__ __forceinline__ f32x16_t mma(T a, T b, f32x16_t c)
     {
         // formats 0/0 = E4M3 for A and B; scale exponent 127 = 2^0
@@ -472,17 +484,19 @@ stream_topk_kernel(StreamArgs a)
     constexpr int QB = kWaves * QW;                  // positions per block
     constexpr int KT = kKeysPerTile;
     constexpr int NDS = D / O::KSTEP;                // K steps per half tile
-    constexpr int ROWB = D * O::ESZ + 16;            // padded LDS key row
+    constexpr int ROWB = D * O::ESZ;                 // LDS key row (swizzled, unpadded)
+    constexpr int NC = ROWB / 16;                    // 16-byte chunks per key row
     constexpr int TILEB = KT * ROWB;
-    constexpr int RV = D * O::ESZ / 16;              // 16-byte vectors per key row
-    constexpr int NV = KT * RV;                      // vectors per tile
-    constexpr int VPT = (NV + kThreads - 1) / kThreads;
+    constexpr int NDMA = TILEB / 1024;               // 1 KB wave DMA loads per tile
+    constexpr int NDMA_W = (NDMA + kWaves - 1) / kWaves;
+    constexpr int NBUF = 3;                          // LDS ring of key tiles
+    constexpr int PD = NBUF - 1;                     // tiles loaded ahead
     constexpr int NB = 512 / QW;                     // threshold bins per position
     constexpr int HEAD = NB / 8 > 1 ? NB / 8 : 1;    // headroom above the max seen
     constexpr int UPD = 64;                          // appends between refreshes
 
-    __shared__ __attribute__((aligned(16))) unsigned char s_k[2][TILEB];
-    __shared__ float s_ks[2][KT];
+    __shared__ __attribute__((aligned(16))) unsigned char s_k[NBUF][TILEB];
+    __shared__ float s_ks[NBUF][KT];
     __shared__ uint32_t s_rhist[kWaves][256];       // radix select scratch
     __shared__ uint32_t s_th[kWaves][QW * NB];      // threshold histograms
 
@@ -618,96 +632,147 @@ stream_topk_kernel(StreamArgs a)
             }
         };
 
-        // ---- key tiles: global -> registers -> LDS (double buffered)
+        // ---- key tiles: direct global -> LDS loads into a ring of NBUF
+        // buffers, NBUF-1 tiles ahead.  Row r of a tile keeps its 16-byte
+        // chunk c at chunk c ^ (r % NC), so the 32 lanes reading one chunk of
+        // 32 different rows hit distinct LDS banks; the swizzle is applied
+        // through each lane's source address.
         const unsigned char *kbase = a.k + b * a.T * (D * O::ESZ);
         const float *ksbase = FP8 ? a.k_scale + b * a.T : nullptr;
-        u32x4_t pre[VPT];
-        float pks = 0.f;
-        auto load_tile = [&](int it) {
+        // DMA loads this wave issues per tile (the vmcnt it waits on)
+        const int my_dma = (NDMA > wave ? (NDMA - wave + kWaves - 1) / kWaves : 0) +
+                           ((FP8 && wave == 0) ? 1 : 0);
+        auto dma_tile = [&](int it, int buf) {
+            const int64_t row0 = int64_t(it) * KT;
 #pragma unroll
-            for (int v = 0; v < VPT; ++v) {
-                const int vi = tid + v * kThreads;
-                pre[v] = u32x4_t{0, 0, 0, 0};
-                if (vi < NV) {
-                    const int64_t key = int64_t(it) * KT + vi / RV;
-                    if (key < a.T)
-                        pre[v] = *reinterpret_cast<const u32x4_t *>(
-                            kbase + key * (D * O::ESZ) + (vi % RV) * 16);
+            for (int v = 0; v < NDMA_W; ++v) {
+                const int j = wave + v * kWaves;          // 1 KB block of the tile
+                if (j < NDMA) {
+                    const int off = j * 1024 + lane * 16;  // LDS byte of this lane
+                    const int r = off / ROWB;
+                    const int c = ((off % ROWB) / 16) ^ (r % NC);
+                    int64_t key = row0 + r;
+                    key = key < a.T ? key : a.T - 1;      // rows past T are never used
+                    __builtin_amdgcn_global_load_lds(
+                        kbase + key * ROWB + c * 16,
+                        (__attribute__((address_space(3))) void *)&s_k[buf][j * 1024], 16, 0, 0);
                 }
             }
             if constexpr (FP8) {
-                const int64_t key = int64_t(it) * KT + tid;
-                pks = (tid < KT && key < a.T) ? ksbase[key] : 0.f;
-            }
-        };
-        auto store_tile = [&](int buf) {
-#pragma unroll
-            for (int v = 0; v < VPT; ++v) {
-                const int vi = tid + v * kThreads;
-                if (vi < NV)
-                    *reinterpret_cast<u32x4_t *>(&s_k[buf][(vi / RV) * ROWB + (vi % RV) * 16]) = pre[v];
-            }
-            if constexpr (FP8)
-                if (tid < KT) s_ks[buf][tid] = pks;
-        };
-        // the MFMAs of the wave's rows against both 32-key halves of LDS tile buf
-        f32x16_t acc[2][2];
-        auto mma_tile = [&](int buf) {
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const unsigned char *kb = &s_k[buf][(ks * 32 + col) * ROWB + half * O::LANE_BYTES];
-#pragma unroll
-                for (int ds = 0; ds < NDS; ++ds) {
-                    const OpT bk = O::load(kb + ds * O::KSTEP * O::ESZ);
-#pragma unroll
-                    for (int hb = 0; hb < 2; ++hb)
-                        acc[ks][hb] = O::mma(qa[hb][ds], bk, ds == 0 ? f32x16_t{} : acc[ks][hb]);
+                if (wave == 0) {
+                    int64_t key = row0 + lane;
+                    key = key < a.T ? key : a.T - 1;
+                    __builtin_amdgcn_global_load_lds(
+                        ksbase + key, (__attribute__((address_space(3))) void *)&s_ks[buf][0], 4, 0, 0);
                 }
             }
         };
-        // epilogue of the accumulated tile it, then the filter and appends
-        auto epilogue = [&](int it, float ksv) {
-            float p0[E::NP], p1[E::NP], sc[QW];
-            E::partial(acc[0], wr, p0);
-            E::partial(acc[1], wr, p1);
-            E::combine(p0, p1, sc);
+        // Waits until at most `outstanding` of this wave's loads are in flight
+        // (the most recent ones) and its LDS accesses are done, then joins
+        // the workgroup barrier.
+        auto sync_tiles = [&](int outstanding) {
+            // s_waitcnt: vmcnt = outstanding (0..15), lgkmcnt = 0, expcnt = 7
+            switch (outstanding) {
+            case 0: __builtin_amdgcn_s_waitcnt(0x0070); break;
+            case 1: __builtin_amdgcn_s_waitcnt(0x0071); break;
+            case 2: __builtin_amdgcn_s_waitcnt(0x0072); break;
+            case 3: __builtin_amdgcn_s_waitcnt(0x0073); break;
+            case 4: __builtin_amdgcn_s_waitcnt(0x0074); break;
+            case 5: __builtin_amdgcn_s_waitcnt(0x0075); break;
+            case 6: __builtin_amdgcn_s_waitcnt(0x0076); break;
+            case 7: __builtin_amdgcn_s_waitcnt(0x0077); break;
+            case 8: __builtin_amdgcn_s_waitcnt(0x0078); break;
+            default: __builtin_amdgcn_s_waitcnt(0x0079); break;
+            }
+            __builtin_amdgcn_s_barrier();
+        };
+        // loads this wave issued after those of tile t+1, once the tiles up
+        // to min(t + PD, ntiles - 1) are staged
+        auto later_loads = [&](int t, int ntiles) {
+            const int last = t + PD < ntiles - 1 ? t + PD : ntiles - 1;
+            return last > t + 1 ? my_dma * (last - t - 1) : 0;
+        };
+        // the 2*NDS MFMAs of the wave's rows against 32-key half ks of tile buf
+        f32x16_t acc[2];
+        auto mma_half = [&](int buf, int ks) {
+            const int r = ks * 32 + col;
+            const unsigned char *kb = &s_k[buf][r * ROWB];
+#pragma unroll
+            for (int ds = 0; ds < NDS; ++ds) {
+                const int c0 = (ds * O::KSTEP * O::ESZ + half * O::LANE_BYTES) / 16;
+                const OpT bk = O::load_swz(kb, c0, r % NC);
+#pragma unroll
+                for (int hb = 0; hb < 2; ++hb)
+                    acc[hb] = O::mma(qa[hb][ds], bk, ds == 0 ? f32x16_t{} : acc[hb]);
+            }
+            // operand reads one K step ahead of their MFMAs
+            constexpr int RD = FP8 ? 2 : 1;  // LDS reads per K step
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * RD, 0);
+#pragma unroll
+            for (int st = 0; st < NDS - 2; ++st) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        };
+        // scores of tile it from the two half partials; filter and append
+        auto finish = [&](const float (&ha)[E::NP], const float (&hb)[E::NP], int it, float ksv) {
+            float sc[QW];
+            E::combine(ha, hb, sc);
             if constexpr (FP8)
 #pragma unroll
                 for (int qi = 0; qi < QW; ++qi) sc[qi] *= ksv;
             consume(sc, it);
         };
 
-        // Waves 0-3 score tile i and then run its epilogue; waves 4-7 (the
-        // second wave of each SIMD) first finish the epilogue of tile i-1 and
-        // then score tile i.  The two waves sharing a SIMD are thus half a
-        // period apart: one issues MFMAs while the other runs VALU work.
+        // Waves 0-3 run, per tile i: MFMA(half 0), its epilogue, MFMA(half 1),
+        // its epilogue, the filter.  Waves 4-7 (the second wave of each SIMD)
+        // run the same steps half a tile later: they open tile i with the
+        // epilogue and filter of tile i-1 and close it with MFMA(half 1),
+        // whose accumulators they carry over the barrier.  The two waves of a
+        // SIMD thus alternate between matrix-core and VALU work.
         const bool lagging = wave >= kWaves / 2;
         const int ntiles = (n_hi + KT - 1) / KT;
-        if (ntiles > 0) {
-            load_tile(0);
-            store_tile(0);
-        }
+        // every wave is past its last read of the ring (previous block)
         __syncthreads();
+        for (int t = 0; t < PD && t < ntiles; ++t) dma_tile(t, t);
+        sync_tiles(later_loads(-1, ntiles));
         float ksv_prev = 1.f;
+        float h0[E::NP], h1[E::NP];
 #pragma unroll 1
         for (int it = 0; it < ntiles; ++it) {
-            const int buf = it & 1;
-            const bool more = it + 1 < ntiles;
-            if (more) load_tile(it + 1);
+            const int buf = it % NBUF;
             float ksv = 1.f;
             if constexpr (FP8) ksv = s_ks[buf][lane];
+            // Each wave stages its share of tile it+PD (over tile it-1, which
+            // every wave has finished) right after its own filter step: the
+            // LDS writes of a filter step wait for this wave's outstanding
+            // loads, and these are then always at least an iteration old.
+            const bool stage = it + PD < ntiles;
             if (!lagging) {
-                mma_tile(buf);
-                epilogue(it, ksv);
+                mma_half(buf, 0);
+                E::partial(acc, wr, h0);
+                mma_half(buf, 1);
+                E::partial(acc, wr, h1);
+                finish(h0, h1, it, ksv);
+                if (stage) dma_tile(it + PD, (it + PD) % NBUF);
             } else {
-                if (it > 0) epilogue(it - 1, ksv_prev);
-                mma_tile(buf);
+                if (it > 0) {
+                    E::partial(acc, wr, h1);
+                    finish(h0, h1, it - 1, ksv_prev);
+                }
+                if (stage) dma_tile(it + PD, (it + PD) % NBUF);
+                mma_half(buf, 0);
+                E::partial(acc, wr, h0);
+                mma_half(buf, 1);
             }
             ksv_prev = ksv;
-            if (more) store_tile(buf ^ 1);
-            __syncthreads();
+            sync_tiles(later_loads(it, ntiles));
         }
-        if (lagging && ntiles > 0) epilogue(ntiles - 1, ksv_prev);
+        if (lagging && ntiles > 0) {
+            E::partial(acc, wr, h1);
+            finish(h0, h1, ntiles - 1, ksv_prev);
+        }
 
         // ---- final merge and (unsorted, key-ordered) output rows
 #pragma unroll 1
