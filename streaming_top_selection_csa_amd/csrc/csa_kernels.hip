@@ -350,6 +350,38 @@ struct Hist {
         return __shfl(b, L);
     }
 
+    // As top_bin; *above receives the count in the bins above the result.
+    static __device__ __forceinline__ int top_bin_above(const uint32_t *h, int need, int lane,
+                                                        uint32_t *above)
+    {
+        uint32_t c[PER];
+        uint32_t cl = 0u;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int b = NB - 1 - (lane * PER + j);
+            c[j] = b >= 0 ? h[b] : 0u;
+            cl += c[j];
+        }
+        const uint32_t pre = wave_prefix_sum(cl);
+        const uint64_t bal = __ballot(pre >= uint32_t(need));
+        if (bal == 0) return -1;
+        const int L = __ffsll(static_cast<unsigned long long>(bal)) - 1;
+        uint32_t acc = pre - cl;
+        int b = NB - 1 - (lane * PER + PER - 1);
+        uint32_t ab = acc;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            if (acc + c[j] >= uint32_t(need)) {
+                b = NB - 1 - (lane * PER + j);
+                ab = acc;
+                break;
+            }
+            acc += c[j];
+        }
+        *above = __shfl(ab, L);
+        return __shfl(b, L);
+    }
+
     static __device__ __forceinline__ void zero_below(uint32_t *h, int b, int lane)
     {
 #pragma unroll
@@ -410,6 +442,169 @@ __device__ __noinline__ void hist_recount(uint32_t *h, int hbase, const uint32_t
         }
     }
     wave_lds_sync();
+}
+
+// Radix select, in LDS, of the `need` best of n candidates (cu, ci) that
+// share the top 16 bits `g` of their order keys; writes them to out[0..need)
+// (candidates kept in their LDS order, i.e. ascending key among ties).
+__device__ __forceinline__ void select_candidates(const uint32_t *cu, const int32_t *ci, int n,
+                                                  int need, uint32_t g, uint32_t *rhist,
+                                                  int32_t *oi, float *os, int lane)
+{
+    uint32_t prefix = g << 16, pmask = 0xFFFF0000u;
+    int kk = need;
+#pragma unroll 1
+    for (int shift = 8; shift >= 0; shift -= 8) {
+        for (int i = lane; i < 256; i += 64) rhist[i] = 0u;
+        wave_lds_sync();
+        for (int e = lane; e < n; e += 64) {
+            const uint32_t u = cu[e];
+            if ((u & pmask) == prefix) atomicAdd(&rhist[(u >> shift) & 255u], 1u);
+        }
+        wave_lds_sync();
+        // lane 0 owns the top digits: prefix sum over reversed digit order
+        const uint32_t r0 = rhist[255 - 4 * lane], r1 = rhist[254 - 4 * lane];
+        const uint32_t r2 = rhist[253 - 4 * lane], r3 = rhist[252 - 4 * lane];
+        const uint32_t rl = r0 + r1 + r2 + r3;
+        const uint32_t pre = wave_prefix_sum(rl);
+        const uint32_t want = uint32_t(kk);
+        const uint64_t bal = __ballot(pre >= want);
+        const int L = __ffsll(static_cast<unsigned long long>(bal)) - 1;
+        uint32_t acc = pre - rl;
+        int d = 252 - 4 * lane;
+        uint32_t ab = acc;
+        if (acc + r0 >= want) {
+            d = 255 - 4 * lane;
+        } else if (acc + r0 + r1 >= want) {
+            d = 254 - 4 * lane;
+            ab = acc + r0;
+        } else if (acc + r0 + r1 + r2 >= want) {
+            d = 253 - 4 * lane;
+            ab = acc + r0 + r1;
+        } else {
+            ab = acc + r0 + r1 + r2;
+        }
+        d = __shfl(d, L);
+        ab = __shfl(ab, L);
+        kk -= int(ab);
+        prefix |= uint32_t(d) << shift;
+        pmask |= 0xFFu << shift;
+        wave_lds_sync();
+    }
+    int wpos = 0, eq_seen = 0;
+#pragma unroll 1
+    for (int base = 0; base < n; base += 64) {
+        const int e = base + lane;
+        const bool valid = e < n;
+        const uint32_t u = valid ? cu[e] : 0u;
+        const bool gt = valid && u > prefix;
+        const bool eq = valid && u == prefix;
+        const uint64_t meq = __ballot(eq);
+        const bool keep = gt || (eq && eq_seen + lanes_below(meq) < kk);
+        const uint64_t mk = __ballot(keep);
+        if (keep) {
+            const int p = wpos + lanes_below(mk);
+            oi[p] = ci[e];
+            os[p] = key_to_float(u);
+        }
+        wpos += __popcll(mk);
+        eq_seen += __popcll(meq);
+    }
+}
+
+// Writes the min(k, cnt) best entries of a position's log (in any order)
+// and the padding to its output row.  The threshold histogram names the
+// bin holding the k-th best and counts what lies above it, so one pass
+// over the log writes every entry above that bin and gathers the bin's
+// entries into LDS (cu/ci, cap entries), where a short radix select picks
+// the rest.  Falls back to the exact merge of the whole log when the bin
+// is the clamped bottom bin, holds more than cap entries, or the counts
+// disagree.
+template <int NB>
+__device__ __noinline__ void final_select(uint32_t *lu, int32_t *li, int cnt, int k,
+                                          const uint32_t *h, int hbase, uint32_t *cu,
+                                          int32_t *ci, int cap, uint32_t *rhist,
+                                          int32_t *oi, float *os, int lane)
+{
+    wave_global_sync();
+    wave_lds_sync();
+    int wpos = 0;
+    bool done = false;
+    if (cnt <= k) {
+        // every log entry is a result (see the filter rule)
+#pragma unroll 1
+        for (int e = lane; e < cnt; e += 64) {
+            oi[e] = li[e];
+            os[e] = key_to_float(lu[e]);
+        }
+        wpos = cnt;
+        done = true;
+    } else {
+        uint32_t above = 0u;
+        const int b = Hist<NB>::top_bin_above(h, k, lane, &above);
+        const int g = hbase + b;
+        const uint32_t nb = b >= 0 ? h[b] : 0u;
+        if (b > 0 && g > 0 && g < 65535 && nb <= uint32_t(cap) && int(above) < k) {
+            wpos = 0;
+            const uint32_t lo = uint32_t(g) << 16, hi = uint32_t(g + 1) << 16;
+            int cpos = 0;
+#pragma unroll 1
+            for (int base = 0; base < cnt; base += 64 * kBatch) {
+                uint32_t u[kBatch];
+                int32_t id[kBatch];
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j) {
+                    const int e = base + 64 * j + lane;
+                    u[j] = e < cnt ? lu[e] : 0u;
+                    id[j] = e < cnt ? li[e] : 0;
+                }
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j) {
+                    const bool valid = base + 64 * j + lane < cnt;
+                    const bool sel = valid && u[j] >= hi;
+                    const bool cand = valid && u[j] >= lo && u[j] < hi;
+                    const uint64_t ms = __ballot(sel);
+                    const uint64_t mc = __ballot(cand);
+                    const int ps = wpos + lanes_below(ms);
+                    const int pc = cpos + lanes_below(mc);
+                    if (sel && ps < k) {
+                        oi[ps] = id[j];
+                        os[ps] = key_to_float(u[j]);
+                    }
+                    if (cand && pc < cap) {
+                        cu[pc] = u[j];
+                        ci[pc] = id[j];
+                    }
+                    wpos += __popcll(ms);
+                    cpos += __popcll(mc);
+                }
+            }
+            wave_lds_sync();
+            // the counts of this pass decide: with wpos < k <= wpos + cpos
+            // the result is every entry above the bin plus the best k - wpos
+            // of the bin (ties in log order, i.e. by ascending key)
+            if (wpos < k && wpos + cpos >= k && cpos <= cap) {
+                select_candidates(cu, ci, cpos, k - wpos, uint32_t(g), rhist, oi + wpos,
+                                  os + wpos, lane);
+                wpos = k;
+                done = true;
+            }
+        }
+    }
+    if (!done) {
+        merge_log(lu, li, cnt, k, rhist, lane);
+#pragma unroll 1
+        for (int e = lane; e < k; e += 64) {
+            oi[e] = li[e];
+            os[e] = key_to_float(lu[e]);
+        }
+        wpos = k;
+    }
+#pragma unroll 1
+    for (int e = wpos + lane; e < k; e += 64) {
+        oi[e] = -1;
+        os[e] = -__builtin_inff();
+    }
 }
 
 // ------------------------------------------------------------ score epilogue
@@ -774,30 +969,20 @@ stream_topk_kernel(StreamArgs a)
             finish(h0, h1, ntiles - 1, ksv_prev);
         }
 
-        // ---- final merge and (unsorted, key-ordered) output rows
+        // ---- final selection into the (unsorted) output rows; the key ring
+        // is idle until the next block's first barrier and serves as each
+        // wave's candidate buffer
+        constexpr int CAP = NBUF * TILEB / kWaves / 8;
+        uint32_t *const cu = reinterpret_cast<uint32_t *>(&s_k[0][0] + wave * (NBUF * TILEB / kWaves));
+        int32_t *const ci = reinterpret_cast<int32_t *>(cu + CAP);
 #pragma unroll 1
         for (int qi = 0; qi < QW; ++qi) {
             const int64_t pos = wp0 + qi;
             if (pos >= a.S) break;
-            uint32_t *lu = log_u + qi * a.log_cap;
-            int32_t *li = log_i + qi * a.log_cap;
-            int c = cnt[qi];
-            if (c > a.topk) {
-                merge_log(lu, li, c, a.topk, rhist, lane);
-                c = a.topk;
-            } else {
-                wave_global_sync();
-            }
             const int64_t row = (b * a.S + pos) * a.topk;
-            for (int e = lane; e < a.topk; e += 64) {
-                if (e < c) {
-                    a.out_idx[row + e] = li[e];
-                    a.out_score[row + e] = key_to_float(lu[e]);
-                } else {
-                    a.out_idx[row + e] = -1;
-                    a.out_score[row + e] = -__builtin_inff();
-                }
-            }
+            final_select<NB>(log_u + qi * a.log_cap, log_i + qi * a.log_cap, cnt[qi], a.topk,
+                             &s_th[wave][qi * NB], hbase[qi], cu, ci, CAP, rhist,
+                             a.out_idx + row, a.out_score + row, lane);
         }
     }
 }
