@@ -1,0 +1,148 @@
+"""C-ABI checks that need no GPU: exported symbols, planning, validation.
+
+Every entry point validates its arguments before it touches the device,
+so invalid calls return their documented status here too.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import streaming_top_selection_csa_amd as csa
+from streaming_top_selection_csa_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa_index.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return csa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(B.EXPORTS)
+
+
+def test_library_exports_every_declared_function(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def opts(**kw):
+    kw.setdefault("num_cus", 256)
+    return B.make_options(**kw)
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4):
+        assert csa.status_string(code)
+    assert csa.status_string(12345) == "unknown status"
+
+
+@pytest.mark.parametrize("S,T", [(65536, 16384), (262144, 65536), (1048576, 262144), (1000, 3)])
+def test_workspace_independent_of_S_and_T(lib, S, T):
+    ref = csa.plan_query(csa.make_desc(1, 65536, 16384, 64, 128), 4, 2048, opts())
+    info = csa.plan_query(csa.make_desc(1, S, T, 64, 128), 4, 2048, opts())
+    if (S + 7) // 8 >= 256:  # enough blocks to fill the 256-workgroup grid
+        assert info.workspace_bytes == ref.workspace_bytes
+    assert info.workspace_bytes <= ref.workspace_bytes
+    assert info.n_blocks == (S + info.queries_per_block - 1) // info.queries_per_block
+
+
+def test_plan_fields(lib):
+    info = csa.plan_query(csa.make_desc(2, 1000, 250, 4, 32), 4, 64, opts())
+    assert info.queries_per_block == 8 * 64 // 4           # 8 waves x 64 rows / H
+    assert info.n_blocks == 2 * ((1000 + 127) // 128)
+    assert info.grid == min(info.n_blocks, 256)
+    assert info.keys_per_tile == 64
+    assert info.chunk_keys == 1024                          # default: 4k within [1024, 8192]
+    assert info.log_capacity == 64 + 1024
+    big = csa.plan_query(csa.make_desc(1, 4096, 1024, 64, 128), 4, 2048, opts())
+    assert big.chunk_keys == 8192 and big.log_capacity == 2048 + 8192
+    c = csa.plan_query(csa.make_desc(1, 4096, 1024, 64, 128), 4, 100, opts(chunk_keys=100))
+    assert c.chunk_keys == 128                              # rounded up to the tile
+    assert csa.workspace_bytes(csa.make_desc(1, 4096, 1024, 64, 128), 4, 2048, opts()) == \
+        big.workspace_bytes
+    assert big.workspace_bytes == 256 * 8 * 1 * (2048 + 8192) * 8
+
+
+def bad(lib, desc, m=4, k=8, opt=None):
+    info = B.CsaPlanInfo()
+    o = opt if opt is not None else opts()
+    return lib.csa_plan_query(ctypes.byref(desc) if desc is not None else None, m, k,
+                              ctypes.byref(o), ctypes.byref(info))
+
+
+def test_validation_errors(lib):
+    ok = csa.make_desc(1, 100, 25, 64, 128)
+    assert bad(lib, ok) == B.CSA_OK
+    assert bad(lib, None) == B.CSA_ERR_INVALID_ARG
+    assert bad(lib, ok, m=0) == B.CSA_ERR_INVALID_ARG
+    assert bad(lib, ok, k=0) == B.CSA_ERR_INVALID_ARG
+    assert bad(lib, ok, k=16385) == B.CSA_ERR_UNSUPPORTED
+    assert bad(lib, csa.make_desc(0, 100, 25, 64, 128)) == B.CSA_ERR_INVALID_ARG
+    assert bad(lib, csa.make_desc(1, -1, 25, 64, 128)) == B.CSA_ERR_INVALID_ARG
+    assert bad(lib, csa.make_desc(1, 100, -1, 64, 128)) == B.CSA_ERR_INVALID_ARG
+    assert bad(lib, csa.make_desc(1, 100, 25, 3, 128)) == B.CSA_ERR_UNSUPPORTED
+    assert bad(lib, csa.make_desc(1, 100, 25, 128, 128)) == B.CSA_ERR_UNSUPPORTED
+    assert bad(lib, csa.make_desc(1, 100, 25, 64, 48)) == B.CSA_ERR_UNSUPPORTED
+    assert bad(lib, csa.make_desc(1, 100, 25, 64, 32, B.CSA_FP8_E4M3FN, 1, 1)) == B.CSA_ERR_UNSUPPORTED
+    assert bad(lib, csa.make_desc(1, 100, 25, 64, 128, 7)) == B.CSA_ERR_INVALID_ARG
+    assert bad(lib, csa.make_desc(1, 100, 25, 64, 128, B.CSA_FP8_E4M3FN)) == B.CSA_ERR_INVALID_ARG
+    assert bad(lib, csa.make_desc(1, 100, 25, 64, 128, B.CSA_BF16, 16, 0)) == B.CSA_ERR_INVALID_ARG
+    d = csa.make_desc(1, 100, 25, 64, 128)
+    d.reserved0 = 1
+    assert bad(lib, d) == B.CSA_ERR_INVALID_ARG
+    assert bad(lib, ok, opt=opts(row_offset=-1)) == B.CSA_ERR_INVALID_ARG
+    assert bad(lib, ok, opt=opts(chunk_keys=-5)) == B.CSA_ERR_INVALID_ARG
+    o = opts()
+    o.num_cus = -1
+    assert bad(lib, ok, opt=o) == B.CSA_ERR_INVALID_ARG
+    assert lib.csa_plan_query(ctypes.byref(ok), 4, 8, ctypes.byref(opts()), None) == \
+        B.CSA_ERR_INVALID_ARG
+    assert lib.csa_workspace_bytes(ctypes.byref(csa.make_desc(1, 100, 25, 3, 128)), 4, 8,
+                                   ctypes.byref(opts())) == 0
+
+
+def call_index(lib, q=16, w=16, k_cmp=16, oi=16, os_=16, desc=None, opt=None, m=4, k=8):
+    desc = desc or csa.make_desc(1, 100, 25, 64, 128)
+    opt = opt or opts()
+    return lib.csa_index_ex(q, w, k_cmp, ctypes.byref(desc), m, k, oi, os_,
+                            ctypes.byref(opt), None)
+
+
+def test_index_rejects_before_touching_the_device(lib):
+    # dummy (never dereferenced) addresses: every call below must fail validation
+    assert call_index(lib, q=None) == B.CSA_ERR_INVALID_ARG
+    assert call_index(lib, w=None) == B.CSA_ERR_INVALID_ARG
+    assert call_index(lib, k_cmp=None) == B.CSA_ERR_INVALID_ARG
+    assert call_index(lib, oi=None) == B.CSA_ERR_INVALID_ARG
+    assert call_index(lib, os_=None) == B.CSA_ERR_INVALID_ARG
+    assert call_index(lib, q=24) == B.CSA_ERR_INVALID_ARG          # q not 16-byte aligned
+    assert call_index(lib, k_cmp=40) == B.CSA_ERR_INVALID_ARG
+    assert call_index(lib, w=18) == B.CSA_ERR_INVALID_ARG
+    assert call_index(lib, k=0) == B.CSA_ERR_INVALID_ARG
+    short = opts(workspace=256, workspace_bytes=1024)
+    assert call_index(lib, opt=short) == B.CSA_ERR_WORKSPACE
+    misaligned = opts(workspace=272, workspace_bytes=1 << 40)
+    assert call_index(lib, opt=misaligned) == B.CSA_ERR_WORKSPACE
+    # nothing to do: no rows
+    assert call_index(lib, q=None, w=None, oi=None, os_=None,
+                      desc=csa.make_desc(1, 0, 25, 64, 128)) == B.CSA_OK
+
+
+def test_binding_refuses_host_tensors(lib):
+    import torch
+    q = torch.zeros((1, 8, 64, 128), dtype=torch.bfloat16)
+    w = torch.zeros((1, 8, 64), dtype=torch.float32)
+    k = torch.zeros((1, 2, 128), dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        csa.index(q, w, k, 4, 2)
