@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libcsa_index.so")
 OBJDIR = os.path.join(HERE, "_build")
 
-SOURCES = ["csa_plan.cpp", "csa_kernels.hip", "csa_abi.cpp"]
+SOURCES = ["csa_plan.cpp", "csa_kernels.hip", "csa_sort.hip", "csa_abi.cpp"]
 
 ARCH = "gfx950"
 FLAGS = [

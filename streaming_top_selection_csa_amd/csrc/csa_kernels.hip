@@ -4,7 +4,8 @@
 // Top-k (Abstract) computes, per query position, lightning-indexer scores
 // over the compressed keys and keeps the top-k, with a chunked
 // partition-merge driver that never materialises the [B,S,H_I,T] tensor.
-// Here that is one persistent scoring kernel plus a row sort:
+// Here that is one persistent scoring kernel (this file) plus a row sort
+// (csa_sort.hip):
 //
 //   stream_topk_kernel  Each wave owns 64 (position, head) rows of q, held in
 //       VGPRs as MFMA A-operands.  The workgroup stages 64-key tiles of k_cmp
@@ -18,13 +19,14 @@
 //       k-th best (score desc, index asc), compacts the log to exactly the
 //       running top-k in key order (the merge step), and raises the
 //       threshold.  At the end the log is the exact top-min(k, n_vis) set.
-//   sort_rows_kernel  Orders every output row by (score desc, index asc)
-//       with a bitonic sort in LDS and leaves padding (-1, -inf) last.
+//   row sort  Orders every output row by (score desc, index asc) and
+//       leaves padding (-1, -inf) last.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 
 #include "csa_kernels.hpp"
+#include "csa_order_key.hpp"
 
 namespace csa {
 
@@ -34,19 +36,6 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------------ helpers
-
-// Monotone map float -> uint32 (larger float -> larger key), -0 == +0.
-__device__ __forceinline__ uint32_t order_key(float f)
-{
-    uint32_t b = __float_as_uint(f);
-    if (b == 0x80000000u) b = 0u;
-    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-
-__device__ __forceinline__ float key_to_float(uint32_t u)
-{
-    return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
-}
 
 // max(x, 0) for finite x as one signed-integer max on the bit pattern:
 // negative floats (and -0) have the sign bit set, i.e. are negative ints.
@@ -987,52 +976,6 @@ stream_topk_kernel(StreamArgs a)
     }
 }
 
-// ------------------------------------------------------------------ row sort
-
-// Sorts each row of k (index, score) pairs by (score desc, index asc);
-// padding (-1, -inf) sorts last.  pow2 = next power of two >= k entries of
-// 64-bit keys live in dynamic LDS.
-__global__ void __launch_bounds__(256)
-sort_rows_kernel(int32_t *out_idx, float *out_score, int64_t nrows, int k, int pow2)
-{
-    extern __shared__ unsigned long long s_key[];
-    const int tid = threadIdx.x;
-    for (int64_t row = blockIdx.x; row < nrows; row += gridDim.x) {
-        int32_t *ri = out_idx + row * k;
-        float *rs = out_score + row * k;
-        for (int e = tid; e < pow2; e += 256) {
-            unsigned long long key = ~0ull;
-            if (e < k) {
-                const uint32_t u = order_key(rs[e]);
-                key = (static_cast<unsigned long long>(~u) << 32) | uint32_t(ri[e]);
-            }
-            s_key[e] = key;
-        }
-        __syncthreads();
-        for (int size = 2; size <= pow2; size <<= 1) {
-            for (int stride = size >> 1; stride > 0; stride >>= 1) {
-                for (int i = tid; i < pow2 / 2; i += 256) {
-                    const int lo = 2 * stride * (i / stride) + (i % stride);
-                    const int hi = lo + stride;
-                    const bool up = (lo & size) == 0;
-                    const unsigned long long x = s_key[lo], y = s_key[hi];
-                    if ((x > y) == up) {
-                        s_key[lo] = y;
-                        s_key[hi] = x;
-                    }
-                }
-                __syncthreads();
-            }
-        }
-        for (int e = tid; e < k; e += 256) {
-            const unsigned long long key = s_key[e];
-            ri[e] = int32_t(uint32_t(key));
-            rs[e] = key_to_float(~uint32_t(key >> 32));
-        }
-        __syncthreads();
-    }
-}
-
 // ------------------------------------------------------------------ dispatch
 
 template <int H, int D, bool FP8>
@@ -1073,25 +1016,6 @@ hipError_t launch_stream_topk(const Plan &p, const StreamArgs &a, hipStream_t s)
     case 128: return launch_h<128, true>(p.H, a, p.grid, s);
     default: return hipErrorInvalidValue;
     }
-}
-
-hipError_t launch_sort_rows(const Plan &p, int32_t *out_idx, float *out_score, int num_cus,
-                            hipStream_t s)
-{
-    const int64_t nrows = p.B * p.S;
-    if (nrows == 0) return hipSuccess;
-    const int64_t want = int64_t(num_cus) * 8;
-    const int grid = int(nrows < want ? nrows : want);
-    const size_t lds = size_t(p.sort_pow2) * sizeof(unsigned long long);
-    if (lds > 65536) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(sort_rows_kernel),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 int(lds));
-        if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(sort_rows_kernel, dim3(grid), dim3(256), lds, s, out_idx, out_score,
-                       nrows, p.k, p.sort_pow2);
-    return hipGetLastError();
 }
 
 }  // namespace csa

@@ -1,0 +1,167 @@
+// csa_sort.hip -- orders every output row by (score desc, key index asc).
+//
+// The scoring kernel leaves each row's top-k in key order; the result is
+// returned sorted by score, ties by the lower key index, padding (-1, -inf)
+// last.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "csa_kernels.hpp"
+#include "csa_order_key.hpp"
+
+namespace csa {
+
+// ------------------------------------------------------------------ row sort
+
+// Sorts each row of k (index, score) pairs by (score desc, index asc);
+// padding (-1, -inf) sorts last.  pow2 = next power of two >= k entries of
+// 64-bit keys live in dynamic LDS.
+__global__ void __launch_bounds__(256)
+sort_rows_kernel(int32_t *out_idx, float *out_score, int64_t nrows, int k, int pow2)
+{
+    extern __shared__ unsigned long long s_key[];
+    const int tid = threadIdx.x;
+    for (int64_t row = blockIdx.x; row < nrows; row += gridDim.x) {
+        int32_t *ri = out_idx + row * k;
+        float *rs = out_score + row * k;
+        for (int e = tid; e < pow2; e += 256) {
+            unsigned long long key = ~0ull;
+            if (e < k) {
+                const uint32_t u = order_key(rs[e]);
+                key = (static_cast<unsigned long long>(~u) << 32) | uint32_t(ri[e]);
+            }
+            s_key[e] = key;
+        }
+        __syncthreads();
+        for (int size = 2; size <= pow2; size <<= 1) {
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                for (int i = tid; i < pow2 / 2; i += 256) {
+                    const int lo = 2 * stride * (i / stride) + (i % stride);
+                    const int hi = lo + stride;
+                    const bool up = (lo & size) == 0;
+                    const unsigned long long x = s_key[lo], y = s_key[hi];
+                    if ((x > y) == up) {
+                        s_key[lo] = y;
+                        s_key[hi] = x;
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        for (int e = tid; e < k; e += 256) {
+            const unsigned long long key = s_key[e];
+            ri[e] = int32_t(uint32_t(key));
+            rs[e] = key_to_float(~uint32_t(key >> 32));
+        }
+        __syncthreads();
+    }
+}
+
+// Same order, one wave per row for rows of up to 64*E slots: lane l holds
+// slots l*E .. l*E+E-1 as 64-bit keys in registers; a bitonic network runs
+// its stages of stride < E inside each lane and the others across lanes
+// with shuffles, with no workgroup barrier.
+template <int E>
+__global__ void __launch_bounds__(256)
+sort_rows_wave_kernel(int32_t *out_idx, float *out_score, int64_t nrows, int k)
+{
+    constexpr int N = 64 * E;
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    const int64_t nwaves = int64_t(gridDim.x) * 4;
+    for (int64_t row = wave; row < nrows; row += nwaves) {
+        int32_t *ri = out_idx + row * k;
+        float *rs = out_score + row * k;
+        unsigned long long key[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int pos = lane * E + e;
+            key[e] = ~0ull;
+            if (pos < k)
+                key[e] = (static_cast<unsigned long long>(~order_key(rs[pos])) << 32) |
+                         uint32_t(ri[pos]);
+        }
+#pragma unroll
+        for (int size = 2; size <= N; size <<= 1) {
+#pragma unroll
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                if (stride < E) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const int f = e ^ stride;
+                        if (f > e) {
+                            const bool up = ((lane * E + e) & size) == 0;
+                            const unsigned long long x = key[e], y = key[f];
+                            const bool sw = (x > y) == up;
+                            key[e] = sw ? y : x;
+                            key[f] = sw ? x : y;
+                        }
+                    }
+                } else {
+                    const int d = stride / E;  // partner lane distance
+                    const bool lower = (lane & d) == 0;
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const unsigned long long o = __shfl_xor(key[e], d);
+                        const bool up = ((lane * E + e) & size) == 0;
+                        const bool keep_min = lower == up;
+                        const unsigned long long mn = key[e] < o ? key[e] : o;
+                        const unsigned long long mx = key[e] < o ? o : key[e];
+                        key[e] = keep_min ? mn : mx;
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int pos = lane * E + e;
+            if (pos < k) {
+                ri[pos] = int32_t(uint32_t(key[e]));
+                rs[pos] = key_to_float(~uint32_t(key[e] >> 32));
+            }
+        }
+    }
+}
+
+template <int E>
+static hipError_t launch_sort_wave(int64_t nrows, int k, int num_cus, int32_t *out_idx,
+                                   float *out_score, hipStream_t s)
+{
+    const int64_t want = int64_t(num_cus) * 8;
+    const int64_t blocks = (nrows + 3) / 4;
+    const int grid = int(blocks < want ? blocks : want);
+    hipLaunchKernelGGL(sort_rows_wave_kernel<E>, dim3(grid), dim3(256), 0, s, out_idx, out_score,
+                       nrows, k);
+    return hipGetLastError();
+}
+
+hipError_t launch_sort_rows(const Plan &p, int32_t *out_idx, float *out_score, int num_cus,
+                            hipStream_t s)
+{
+    const int64_t nrows = p.B * p.S;
+    if (nrows == 0) return hipSuccess;
+    switch (p.sort_pow2 <= 64 ? 64 : p.sort_pow2) {
+    case 64: return launch_sort_wave<1>(nrows, p.k, num_cus, out_idx, out_score, s);
+    case 128: return launch_sort_wave<2>(nrows, p.k, num_cus, out_idx, out_score, s);
+    case 256: return launch_sort_wave<4>(nrows, p.k, num_cus, out_idx, out_score, s);
+    case 512: return launch_sort_wave<8>(nrows, p.k, num_cus, out_idx, out_score, s);
+    case 1024: return launch_sort_wave<16>(nrows, p.k, num_cus, out_idx, out_score, s);
+    case 2048: return launch_sort_wave<32>(nrows, p.k, num_cus, out_idx, out_score, s);
+    default: break;
+    }
+    const int64_t want = int64_t(num_cus) * 8;
+    const int grid = int(nrows < want ? nrows : want);
+    const size_t lds = size_t(p.sort_pow2) * sizeof(unsigned long long);
+    if (lds > 65536) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(sort_rows_kernel),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 int(lds));
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(sort_rows_kernel, dim3(grid), dim3(256), lds, s, out_idx, out_score,
+                       nrows, p.k, p.sort_pow2);
+    return hipGetLastError();
+}
+
+}  // namespace csa
