@@ -779,13 +779,13 @@ stream_topk_kernel(StreamArgs a)
                 }
                 uint32_t *lu = log_u + qi * a.log_cap;
                 int32_t *li = log_i + qi * a.log_cap;
+                // LDS work first, the log stores last: an LDS write after a
+                // global store waits for that store to complete
                 if (pass) {
-                    const int p = cnt[qi] + lanes_below(mk);
-                    lu[p] = u;
-                    li[p] = key;
                     const int lb = gb - hbase[qi];
                     atomicAdd(&h[lb > 0 ? lb : 0], 1u);
                 }
+                const int p = cnt[qi] + lanes_below(mk);
                 const int added = __popcll(mk);
                 cnt[qi] += added;
                 pend[qi] += added;
@@ -802,6 +802,10 @@ stream_topk_kernel(StreamArgs a)
                         Hist<NB>::zero_below(h, bstar, lane);
                     }
                     pend[qi] = 0;
+                }
+                if (pass) {
+                    lu[p] = u;
+                    li[p] = key;
                 }
                 if (full) {
                     cnt[qi] = compact_log(lu, li, cnt[qi], tau[qi], lane);
