@@ -59,11 +59,26 @@ __device__ __forceinline__ int64_t n_visible(int64_t t, int64_t T, int m)
 }
 
 // LDS traffic of one wave is ordered; this keeps the compiler from moving
-// shared-memory accesses across the point and waits for them to finish.
+// shared-memory accesses across the point and waits for them to finish
+// (lgkmcnt only: a fence would also wait for every global store and key-tile
+// load in flight).
 __device__ __forceinline__ void wave_lds_sync()
 {
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt, expcnt untouched
+    __asm__ volatile("" ::: "memory");
     __builtin_amdgcn_wave_barrier();
+}
+
+// *p += v on an LDS word, without returning the old value.  Inline assembly
+// because the compiler makes an LDS atomic wait for all outstanding vector
+// memory operations (the key-tile loads into LDS and the candidate-log
+// stores) when it cannot prove the addresses disjoint; the counters updated
+// here never share memory with a key tile.  One wave's LDS operations run in
+// issue order, so its later reads of the word see the sum.
+__device__ __forceinline__ void lds_add(uint32_t *p, uint32_t v)
+{
+    const uint32_t a = uint32_t(uintptr_t((__attribute__((address_space(3))) uint32_t *)p));
+    __asm__ volatile("ds_add_u32 %0, %1" : : "v"(a), "v"(v) : "memory");
 }
 
 // Makes global stores of every lane of the wave visible to global loads of
@@ -215,8 +230,8 @@ __device__ __noinline__ uint32_t merge_log(uint32_t *lu, int32_t *li, int n, int
             d = 4 * lane;
             ab = above + c3 + c2 + c1;
         }
-        d = __shfl(d, L);
-        ab = __shfl(ab, L);
+        d = __builtin_amdgcn_readlane(d, L);
+        ab = __builtin_amdgcn_readlane(ab, L);
         kk -= int(ab);
         prefix |= uint32_t(d) << shift;
         pmask |= 0xFFu << shift;
@@ -326,17 +341,16 @@ struct Hist {
         const uint64_t bal = __ballot(pre >= uint32_t(need));
         if (bal == 0) return -1;
         const int L = __ffsll(static_cast<unsigned long long>(bal)) - 1;
+        // in lane L the running count reaches `need` at its first bin j
+        // whose inclusive count does; the counts before it are the j below
         uint32_t acc = pre - cl;
-        int b = NB - 1 - (lane * PER + PER - 1);
+        int below = 0;
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
             acc += c[j];
-            if (acc >= uint32_t(need)) {
-                b = NB - 1 - (lane * PER + j);
-                break;
-            }
+            below += acc < uint32_t(need) ? 1 : 0;
         }
-        return __shfl(b, L);
+        return __builtin_amdgcn_readlane(NB - 1 - (lane * PER + below), L);
     }
 
     // As top_bin; *above receives the count in the bins above the result.
@@ -355,27 +369,25 @@ struct Hist {
         const uint64_t bal = __ballot(pre >= uint32_t(need));
         if (bal == 0) return -1;
         const int L = __ffsll(static_cast<unsigned long long>(bal)) - 1;
-        uint32_t acc = pre - cl;
-        int b = NB - 1 - (lane * PER + PER - 1);
-        uint32_t ab = acc;
+        uint32_t acc = pre - cl, ab = acc;
+        int below = 0;
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
-            if (acc + c[j] >= uint32_t(need)) {
-                b = NB - 1 - (lane * PER + j);
-                ab = acc;
-                break;
-            }
+            const bool under = acc + c[j] < uint32_t(need);
+            below += under ? 1 : 0;
             acc += c[j];
+            ab += under ? c[j] : 0u;
         }
-        *above = __shfl(ab, L);
-        return __shfl(b, L);
+        *above = __builtin_amdgcn_readlane(ab, L);
+        return __builtin_amdgcn_readlane(NB - 1 - (lane * PER + below), L);
     }
 
     static __device__ __forceinline__ void zero_below(uint32_t *h, int b, int lane)
     {
+        const int lim = (b < NB ? b : NB) - lane * PER;  // bins j < lim of this lane
 #pragma unroll
         for (int j = 0; j < PER; ++j)
-            if (lane * PER + j < b && lane * PER + j < NB) h[lane * PER + j] = 0u;
+            if (j < lim) h[lane * PER + j] = 0u;
     }
 
     // Moves the window up by delta > 0 bins; counts falling below it are
@@ -391,20 +403,30 @@ struct Hist {
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
             const int nb = lane * PER + j - delta;
-            if (c[j]) atomicAdd(&h[nb > 0 ? nb : 0], c[j]);
+            if (c[j]) lds_add(&h[nb > 0 ? nb : 0], c[j]);
         }
         wave_lds_sync();
     }
 };
 
+// Maximum over the 64 lanes, wave-uniform: a running maximum on DPP row
+// shifts and row broadcasts leaves the total in lane 63.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_max_step(int v)
+{
+    const int o = __builtin_amdgcn_update_dpp(v, v, CTRL, ROW_MASK, 0xf, false);
+    return o > v ? o : v;
+}
+
 __device__ __forceinline__ int wave_max(int v)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const int o = __shfl_xor(v, off);
-        v = o > v ? o : v;
-    }
-    return v;
+    v = dpp_max_step<0x111, 0xf>(v);  // row_shr:1
+    v = dpp_max_step<0x112, 0xf>(v);  // row_shr:2
+    v = dpp_max_step<0x114, 0xf>(v);  // row_shr:4
+    v = dpp_max_step<0x118, 0xf>(v);  // row_shr:8
+    v = dpp_max_step<0x142, 0xa>(v);  // row_bcast:15
+    v = dpp_max_step<0x143, 0xc>(v);  // row_bcast:31
+    return __builtin_amdgcn_readlane(v, 63);
 }
 
 // Re-counts the k log entries left by an exact merge (window unchanged).
@@ -473,8 +495,8 @@ __device__ __forceinline__ void select_candidates(const uint32_t *cu, const int3
         } else {
             ab = acc + r0 + r1 + r2;
         }
-        d = __shfl(d, L);
-        ab = __shfl(ab, L);
+        d = __builtin_amdgcn_readlane(d, L);
+        ab = __builtin_amdgcn_readlane(ab, L);
         kk -= int(ab);
         prefix |= uint32_t(d) << shift;
         pmask |= 0xFFu << shift;
@@ -686,7 +708,7 @@ stream_topk_kernel(StreamArgs a)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int half = lane >> 5;
     const int col = lane & 31;
     const int G = gridDim.x;
@@ -783,7 +805,7 @@ stream_topk_kernel(StreamArgs a)
                 // global store waits for that store to complete
                 if (pass) {
                     const int lb = gb - hbase[qi];
-                    atomicAdd(&h[lb > 0 ? lb : 0], 1u);
+                    lds_add(&h[lb > 0 ? lb : 0], 1u);
                 }
                 const int p = cnt[qi] + lanes_below(mk);
                 const int added = __popcll(mk);
@@ -808,11 +830,11 @@ stream_topk_kernel(StreamArgs a)
                     li[p] = key;
                 }
                 if (full) {
-                    cnt[qi] = compact_log(lu, li, cnt[qi], tau[qi], lane);
+                    cnt[qi] = __builtin_amdgcn_readfirstlane(compact_log(lu, li, cnt[qi], tau[qi], lane));
                     const int room = a.topk + (a.log_cap - a.topk) / 2;
                     if (cnt[qi] > (room < a.log_cap - KT ? room : a.log_cap - KT)) {
                         // the bins could not separate enough: exact merge
-                        tau[qi] = merge_log(lu, li, cnt[qi], a.topk, rhist, lane);
+                        tau[qi] = __builtin_amdgcn_readfirstlane(merge_log(lu, li, cnt[qi], a.topk, rhist, lane));
                         cnt[qi] = a.topk;
                         hist_recount<NB>(h, hbase[qi], lu, cnt[qi], lane);
                     }
@@ -832,6 +854,9 @@ stream_topk_kernel(StreamArgs a)
                            ((FP8 && wave == 0) ? 1 : 0);
         auto dma_tile = [&](int it, int buf) {
             const int64_t row0 = int64_t(it) * KT;
+            const unsigned char *tb = kbase + row0 * ROWB;  // first key row of the tile
+            // rows past T are never used: they repeat row T-1
+            const int rmax = a.T - row0 - 1 < KT - 1 ? int(a.T - row0 - 1) : KT - 1;
 #pragma unroll
             for (int v = 0; v < NDMA_W; ++v) {
                 const int j = wave + v * kWaves;          // 1 KB block of the tile
@@ -839,10 +864,9 @@ stream_topk_kernel(StreamArgs a)
                     const int off = j * 1024 + lane * 16;  // LDS byte of this lane
                     const int r = off / ROWB;
                     const int c = ((off % ROWB) / 16) ^ (r % NC);
-                    int64_t key = row0 + r;
-                    key = key < a.T ? key : a.T - 1;      // rows past T are never used
+                    const uint32_t src = uint32_t(r < rmax ? r : rmax) * ROWB + uint32_t(c * 16);
                     __builtin_amdgcn_global_load_lds(
-                        kbase + key * ROWB + c * 16,
+                        tb + src,
                         (__attribute__((address_space(3))) void *)&s_k[buf][j * 1024], 16, 0, 0);
                 }
             }
