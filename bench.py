@@ -1,6 +1,7 @@
 """Benchmark of the CSA lightning-indexer top-k on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload s256k] [--no-cpu-baseline]
+    python bench.py --sweep        chunk-size and top-k sweeps at S=65,536
 
 A step is one csa_index call over the whole workload: scoring of every
 causally visible (query, compressed key) pair on the matrix cores, the
@@ -100,6 +101,53 @@ def cpu_baseline(inp, wl, nrows, seed=0):
                        f"fp64 scores + full sort, {dt:.1f} s")}
 
 
+def sweep(csa, args):
+    """Chunk-size and top-k sweeps on the S=65,536 workload.  Each cell is
+    `warmup` untimed calls and `steps` timed ones on resident inputs."""
+    import torch
+    from csa_synth import CHUNK_SWEEP, TOPK_SWEEP, WORKLOADS, make_inputs
+
+    base = WORKLOADS["s64k"]
+    dev = torch.device("cuda:0")
+    inp = make_inputs(base, seed=0, device=dev)
+    cells = [("chunk_keys", c, base.k) for c in CHUNK_SWEEP] + \
+            [("topk", base.k, k) for k in TOPK_SWEEP]
+    flops = 2.0 * base.H * base.D * visible_pairs(base.S, base.n_keys, base.m, base.B)
+    stream = torch.cuda.current_stream(dev)
+    for axis, chunk, k in cells:
+        c = chunk if axis == "chunk_keys" else 0
+        out_idx = torch.empty((base.B, base.S, k), dtype=torch.int32, device=dev)
+        out_score = torch.empty((base.B, base.S, k), dtype=torch.float32, device=dev)
+        ws = csa.workspace_for(inp["q"], inp["k"], base.m, k, c)
+        info = csa.plan_query(csa.make_desc(base.B, base.S, base.n_keys, base.H, base.D), base.m,
+                              k, csa.make_options(chunk_keys=c, num_cus=256))
+        events = csa.HipEvents(args.steps)
+
+        def step(timing=None):
+            csa.index(inp["q"], inp["w"], inp["k"], base.m, k, out_idx=out_idx,
+                      out_score=out_score, chunk_keys=c, workspace=ws, timing=timing,
+                      stream=stream)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(events.pairs[i])
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        kms = sum(events.elapsed_ms(i) for i in range(args.steps)) / args.steps
+        events.close()
+        print(json.dumps({
+            "sweep": axis, "workload": base.name, "S": base.S, "T": base.n_keys,
+            "chunk_keys": info.chunk_keys, "k": k, "steps": args.steps,
+            "ms_per_step": 1e3 * elapsed / args.steps, "scoring_kernel_ms": kms,
+            "queries_per_s": base.B * base.S * args.steps / elapsed,
+            "scoring_tflops": flops / (kms * 1e-3) / 1e12,
+            "workspace_gb": ws.numel() / 1e9}), flush=True)
+        del out_idx, out_score, ws
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -109,6 +157,10 @@ def main():
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--cpu-rows", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the five chunk sizes (k=2048) and the five top-k values "
+                         "(default chunk) on the S=65,536 workload, one JSON line per cell; "
+                         "the GPU tests check every cell against the oracle")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (5 times), to scale "
                          "the HBM byte counters of a profiler run")
@@ -137,6 +189,9 @@ def main():
         print(json.dumps({"copy_bytes": n, "launches": 5}))
         return
     csa.load_library()
+    if args.sweep:
+        sweep(csa, args)
+        return
     wl = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

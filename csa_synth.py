@@ -64,8 +64,10 @@ WORKLOADS = {
                             dist="int", dtype="e4m3fn"),
 }
 
-# chunk sizes (compressed keys) swept on the S = 65,536 workload
+# chunk sizes (compressed keys) and top-k values swept on the S = 65,536
+# workload, five points around its defaults (chunk 8192, k 2048)
 CHUNK_SWEEP = (1024, 2048, 4096, 8192, 16384)
+TOPK_SWEEP = (256, 512, 1024, 2048, 4096)
 
 
 def _generator(device, seed: int, stream: int) -> torch.Generator:

@@ -89,13 +89,15 @@ def compare_tolerant(g_idx, g_score, o_idx, o_score, score_fn, t_rows, T, m, rto
         pair_r.append(np.full(kept, r))
         pair_k.append(gk)
     if not pair_r:
-        return {"max_rel_err": 0.0, "swaps": 0}
+        return {"max_rel_err": 0.0, "swaps": 0, "recall": 1.0, "recall_min": 1.0}
     pr = np.concatenate(pair_r)
     pk = np.concatenate(pair_k)
     s_true = score_fn(pr, pk)
     swaps = 0
     max_rel = 0.0
     off = 0
+    hits = total = 0          # set overlap |G & O| over min(k, n_vis), pooled
+    recall_min = 1.0
     for r in range(nrows):
         kept = int(np.sum(o_idx[r] >= 0))
         if kept == 0:
@@ -112,6 +114,10 @@ def compare_tolerant(g_idx, g_score, o_idx, o_score, score_fn, t_rows, T, m, rto
             max_rel = max(max_rel, float(np.max(err[scale > 0] / scale[scale > 0])))
         gset = set(g_idx[r, :kept].tolist())
         oset = set(o_idx[r, :kept].tolist())
+        common = len(gset & oset)
+        hits += common
+        total += kept
+        recall_min = min(recall_min, common / kept)
         diff = gset ^ oset
         if diff:
             swaps += len(diff) // 2
@@ -124,4 +130,5 @@ def compare_tolerant(g_idx, g_score, o_idx, o_score, score_fn, t_rows, T, m, rto
                 assert np.all(rel <= rtol), (f"t={t_rows[r]}: swapped key {keys[np.argmax(rel)]} "
                                              f"is {float(rel.max())} from the k-th score")
         off += kept
-    return {"max_rel_err": max_rel, "swaps": swaps}
+    return {"max_rel_err": max_rel, "swaps": swaps,
+            "recall": hits / total if total else 1.0, "recall_min": recall_min}

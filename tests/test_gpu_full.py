@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from csa_synth import CHUNK_SWEEP, WORKLOADS, Workload, make_inputs, sample_rows
+from csa_synth import CHUNK_SWEEP, TOPK_SWEEP, WORKLOADS, Workload, make_inputs, sample_rows
 from checker import OracleView, compare_exact, compare_tolerant
 
 pytestmark = pytest.mark.gpu
@@ -57,7 +57,23 @@ def test_s64k_chunk_sweep_bit_identical_and_sampled(csa):
         assert torch.equal(score, ref_score), f"scores differ at chunk {c}"
         del idx, score
     rows = sample_rows(wl.S, wl.m, wl.k, n=256, chunk=CHUNK_SWEEP[0])
-    print(_sample_check(inp, wl, ref_idx, ref_score, rows, exact=False))
+    stats = _sample_check(inp, wl, ref_idx, ref_score, rows, exact=False)
+    print(f"[sweep] chunks {CHUNK_SWEEP} k={wl.k} {stats}", flush=True)
+    assert stats["recall"] > 0.999
+
+
+@pytest.mark.parametrize("k", [k for k in TOPK_SWEEP if k != WORKLOADS["s64k"].k])
+def test_s64k_topk_sweep_sampled(csa, k):
+    """The top-k sweep cells of the S=65,536 workload (k = 2048 is the
+    chunk-sweep test above): sampled rows against the oracle."""
+    wl = WORKLOADS["s64k"].with_(k=k)
+    print(f"\n[case] {wl}", flush=True)
+    inp = make_inputs(wl, seed=0, device="cuda")
+    out_idx, out_score = _run(csa, inp, wl)
+    rows = sample_rows(wl.S, wl.m, wl.k, n=256)
+    stats = _sample_check(inp, wl, out_idx, out_score, rows, exact=False)
+    print(f"[sweep] k={k} {stats}", flush=True)
+    assert stats["recall"] > 0.999
 
 
 @pytest.mark.parametrize("name", ["s256k", "s256k-int"])
