@@ -91,10 +91,11 @@ def cpu_baseline(inp, wl, nrows, seed=0):
     ks = inp["k_scale"][0].cpu().numpy() if "k_scale" in inp else None
     threads = min(len(rows), int(os.environ.get("OMP_NUM_THREADS", "0")) or (os.cpu_count() or 1))
     t0 = time.perf_counter()
-    oracle.topk_rows(q, w, k, rows, wl.m, wl.k, dtype=wl.dtype, q_scale_rows=qs, k_scale=ks,
+    pos = rows + wl.row_offset
+    oracle.topk_rows(q, w, k, pos, wl.m, wl.k, dtype=wl.dtype, q_scale_rows=qs, k_scale=ks,
                      nthreads=threads)
     dt = time.perf_counter() - t0
-    n_vis = np.minimum(wl.n_keys, (rows + 1) // wl.m)
+    n_vis = np.minimum(wl.n_keys, (pos + 1) // wl.m)
     return {"value": len(rows) / dt, "unit": "queries/s", "cores": threads, "kind": "oracle",
             "sample": (f"{len(rows)} seeded uniform rows of {wl.name} (mean visible keys "
                        f"{float(n_vis.mean()):.0f}; workload mean {wl.n_keys / 2:.0f}), "
@@ -155,6 +156,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="s256k")
     ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--key-splits", type=int, default=0,
+                    help="key ranges per query block (0 = automatic, 1 = none)")
     ap.add_argument("--cpu-rows", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
@@ -199,18 +202,23 @@ def main():
     inp = make_inputs(wl, seed=0, device=dev)
     out_idx = torch.empty((wl.B, wl.S, wl.k), dtype=torch.int32, device=dev)
     out_score = torch.empty((wl.B, wl.S, wl.k), dtype=torch.float32, device=dev)
-    ws = csa.workspace_for(inp["q"], inp["k"], wl.m, wl.k, args.chunk)
+    ws = csa.workspace_for(inp["q"], inp["k"], wl.m, wl.k, args.chunk, wl.row_offset,
+                           args.key_splits)
     torch.cuda.synchronize()
     in_bytes = sum(t.numel() * t.element_size() for t in inp.values())
     out_bytes = out_idx.numel() * 4 + out_score.numel() * 4
     ws_bytes = ws.numel()
     events = csa.HipEvents(args.steps)
     stream = torch.cuda.current_stream(dev)
+    plan = csa.plan_query(csa.make_desc(wl.B, wl.S, wl.n_keys, wl.H, wl.D), wl.m, wl.k,
+                          csa.make_options(args.chunk, wl.row_offset,
+                                           key_splits=args.key_splits))
 
     def step(timing=None):
         csa.index(inp["q"], inp["w"], inp["k"], wl.m, wl.k, q_scale=inp.get("q_scale"),
                   k_scale=inp.get("k_scale"), out_idx=out_idx, out_score=out_score,
-                  chunk_keys=args.chunk, workspace=ws, timing=timing, stream=stream)
+                  chunk_keys=args.chunk, row_offset=wl.row_offset, key_splits=args.key_splits,
+                  workspace=ws, timing=timing, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -224,7 +232,7 @@ def main():
     events.close()
     peak_hbm = torch.cuda.max_memory_allocated(dev)
 
-    pairs = visible_pairs(wl.S, wl.n_keys, wl.m, wl.B)
+    pairs = visible_pairs(wl.S, wl.n_keys, wl.m, wl.B, wl.row_offset)
     flops = 2.0 * wl.H * wl.D * pairs
     ms_per_step = 1e3 * elapsed / args.steps
     kernel_avg = sum(kernel_ms) / len(kernel_ms)
@@ -252,7 +260,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "S": wl.S, "T": wl.n_keys, "H_I": wl.H,
                    "d_I": wl.D, "m": wl.m, "k": wl.k, "dist": wl.dist,
-                   "chunk_keys": args.chunk or None},
+                   "row_offset": wl.row_offset, "chunk_keys": args.chunk or None,
+                   "key_splits": plan.key_splits},
         "tflops": step_tflops,
         "mfma_pct_peak": 100.0 * step_tflops / peak,
         "peak_hbm_gb": peak_hbm / 1e9,

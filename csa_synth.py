@@ -44,6 +44,7 @@ class Workload:
     dist: str = "gauss"     # "int" | "gauss"
     dtype: str = "bf16"     # "bf16" | "e4m3fn"
     T: int = -1             # -1: S // m
+    row_offset: int = 0     # absolute position of q row 0
 
     @property
     def n_keys(self) -> int:
@@ -62,6 +63,15 @@ WORKLOADS = {
     "s1m-fp8": Workload("s1m-fp8", B=1, S=1048576, m=4, H=64, D=128, k=2048, dtype="e4m3fn"),
     "s1m-fp8-int": Workload("s1m-fp8-int", B=1, S=1048576, m=4, H=64, D=128, k=2048,
                             dist="int", dtype="e4m3fn"),
+    # short query blocks at the end of a long context (a decode step, or the
+    # last rows of a chunked prefill): 64 positions after 262,080 others, and
+    # 32 sequences with 4 new positions each after 65,532
+    "dec64": Workload("dec64", B=1, S=64, m=4, H=64, D=128, k=2048, T=65536,
+                      row_offset=4 * 65536 - 64),
+    "dec64-int": Workload("dec64-int", B=1, S=64, m=4, H=64, D=128, k=2048, T=65536,
+                          row_offset=4 * 65536 - 64, dist="int"),
+    "dec32x4": Workload("dec32x4", B=32, S=4, m=4, H=64, D=128, k=2048, T=16384,
+                        row_offset=4 * 16384 - 4),
 }
 
 # chunk sizes (compressed keys) and top-k values swept on the S = 65,536

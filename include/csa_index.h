@@ -32,8 +32,8 @@
  *   - Every argument is validated before anything is launched; on any error
  *     nothing is written and a negative csa_status is returned.  No C++
  *     exception crosses this boundary.
- *   - Results are deterministic: bitwise identical across runs, chunk sizes
- *     and launch shapes (no floating-point atomics).
+ *   - Results are deterministic: bitwise identical across runs, chunk sizes,
+ *     key splits and launch shapes (no floating-point atomics).
  */
 #ifndef CSA_INDEX_H
 #define CSA_INDEX_H
@@ -99,6 +99,17 @@ typedef struct {
  *                (hipMallocAsync / hipFreeAsync on `stream`).
  *   timing       Optional pair of hipEvent_t recorded on `stream` right before
  *                and right after the scoring kernel (for measurements).
+ *   key_splits   Number of key ranges each query block is split into (the
+ *                chunks of the partition-merge top-k taken in parallel): each
+ *                range yields the exact top-k of its keys and a merge pass
+ *                selects the top-k of the ranges' lists.  0 = automatic: 1
+ *                while the query blocks fill the device, otherwise enough
+ *                ranges of at least max(k, 1024) keys to fill it (short query
+ *                blocks, decode steps).  n >= 1 asks for n ranges (at most one
+ *                per 64 visible keys).  The partial lists take B*S*G*k*8
+ *                bytes of workspace, capped at 1 GiB by lowering G.  Affects
+ *                speed and workspace only, never the result.
+ *   reserved1    Must be 0.
  */
 typedef struct {
     int32_t chunk_keys;
@@ -107,6 +118,8 @@ typedef struct {
     void *workspace;
     size_t workspace_bytes;
     hipEvent_t timing[2];
+    int32_t key_splits;
+    int32_t reserved1;
 } csa_options;
 
 /* What a call will do; filled by csa_plan_query (host only, no device work). */
@@ -116,7 +129,7 @@ typedef struct {
     int32_t chunk_keys;          /* effective partition (candidate) size   */
     int32_t log_capacity;        /* per-query candidate buffer (entries)    */
     int32_t grid;                /* workgroups of the scoring kernel        */
-    int32_t reserved0;
+    int32_t key_splits;          /* key ranges per query block (G >= 1)     */
     int64_t n_blocks;            /* query blocks over all batch entries     */
     size_t workspace_bytes;      /* device scratch needed                   */
 } csa_plan_info;
@@ -139,8 +152,10 @@ int csa_index_ex(const void *q, const float *w, const void *k_cmp,
                  const csa_options *opt, hipStream_t stream);
 
 /* Device scratch bytes csa_index_ex needs for these arguments (0 on invalid
- * arguments).  Independent of S and T: it scales with the number of resident
- * queries and with k + chunk_keys only. */
+ * arguments).  With one key range (key_splits resolving to 1, always the
+ * case when the query blocks fill the device) it is independent of S and T
+ * and scales with the number of resident queries and k + chunk_keys only;
+ * G > 1 key ranges add B*S*G*k*8 bytes for the partial lists. */
 size_t csa_workspace_bytes(const csa_desc *desc, int32_t m, int32_t k,
                            const csa_options *opt);
 

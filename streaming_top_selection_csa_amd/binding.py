@@ -40,13 +40,14 @@ class CsaDesc(ctypes.Structure):
 class CsaOptions(ctypes.Structure):
     _fields_ = [("chunk_keys", ctypes.c_int32), ("num_cus", ctypes.c_int32),
                 ("row_offset", ctypes.c_int64), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t), ("timing", ctypes.c_void_p * 2)]
+                ("workspace_bytes", ctypes.c_size_t), ("timing", ctypes.c_void_p * 2),
+                ("key_splits", ctypes.c_int32), ("reserved1", ctypes.c_int32)]
 
 
 class CsaPlanInfo(ctypes.Structure):
     _fields_ = [("queries_per_block", ctypes.c_int32), ("keys_per_tile", ctypes.c_int32),
                 ("chunk_keys", ctypes.c_int32), ("log_capacity", ctypes.c_int32),
-                ("grid", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("grid", ctypes.c_int32), ("key_splits", ctypes.c_int32),
                 ("n_blocks", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t)]
 
 
@@ -96,8 +97,9 @@ def make_desc(B, S, T, H, D, dtype=CSA_BF16, q_scale_ptr=0, k_scale_ptr=0) -> Cs
 
 
 def make_options(chunk_keys=0, row_offset=0, num_cus=0, workspace=None, workspace_bytes=0,
-                 timing=(None, None)) -> CsaOptions:
+                 timing=(None, None), key_splits=0) -> CsaOptions:
     opt = CsaOptions()
+    opt.key_splits = int(key_splits)
     opt.chunk_keys = int(chunk_keys)
     opt.num_cus = int(num_cus)
     opt.row_offset = int(row_offset)
@@ -143,8 +145,9 @@ def _check(t: torch.Tensor, name: str, dtype=None):
 def index(q: torch.Tensor, w: torch.Tensor, k_cmp: torch.Tensor, m: int, k: int, *,
           q_scale: Optional[torch.Tensor] = None, k_scale: Optional[torch.Tensor] = None,
           out_idx: Optional[torch.Tensor] = None, out_score: Optional[torch.Tensor] = None,
-          chunk_keys: int = 0, row_offset: int = 0, workspace: Optional[torch.Tensor] = None,
-          timing=None, stream: Optional[torch.cuda.Stream] = None):
+          chunk_keys: int = 0, row_offset: int = 0, key_splits: int = 0,
+          workspace: Optional[torch.Tensor] = None, timing=None,
+          stream: Optional[torch.cuda.Stream] = None):
     """Top-k compressed keys per query position (csa_index_ex).
 
     q [B,S,H,D] bf16 | e4m3fn, w [B,S,H] fp32, k_cmp [B,T,D] same dtype as
@@ -189,7 +192,7 @@ def index(q: torch.Tensor, w: torch.Tensor, k_cmp: torch.Tensor, m: int, k: int,
         _check(workspace, "workspace")
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     opt = make_options(chunk_keys, row_offset, 0, ws_ptr, ws_bytes,
-                       timing if timing is not None else (None, None))
+                       timing if timing is not None else (None, None), key_splits)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     rc = lib.csa_index_ex(q.data_ptr(), w.data_ptr(), k_cmp.data_ptr(), ctypes.byref(desc),
@@ -201,13 +204,13 @@ def index(q: torch.Tensor, w: torch.Tensor, k_cmp: torch.Tensor, m: int, k: int,
 
 
 def workspace_for(q: torch.Tensor, k_cmp: torch.Tensor, m: int, k: int, chunk_keys: int = 0,
-                  row_offset: int = 0) -> torch.Tensor:
+                  row_offset: int = 0, key_splits: int = 0) -> torch.Tensor:
     """A torch-allocated workspace big enough for `index` on these inputs."""
     B, S, H, D = q.shape
     desc = make_desc(B, S, k_cmp.shape[1], H, D, _dtype_code(q),
                      1 if q.dtype == torch.float8_e4m3fn else 0,
                      1 if q.dtype == torch.float8_e4m3fn else 0)
-    n = workspace_bytes(desc, m, k, make_options(chunk_keys, row_offset))
+    n = workspace_bytes(desc, m, k, make_options(chunk_keys, row_offset, key_splits=key_splits))
     if n == 0:
         raise CsaError(CSA_ERR_INVALID_ARG, "csa_workspace_bytes")
     return torch.empty(n, dtype=torch.uint8, device=q.device)

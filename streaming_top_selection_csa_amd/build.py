@@ -16,7 +16,10 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libcsa_index.so")
 OBJDIR = os.path.join(HERE, "_build")
 
-SOURCES = ["csa_plan.cpp", "csa_kernels.hip", "csa_sort.hip", "csa_abi.cpp"]
+# the scoring-kernel instantiations first: they take longest
+SOURCES = ["csa_stream_bf16_d128.hip", "csa_stream_fp8_d128.hip", "csa_stream_bf16_d64.hip",
+           "csa_stream_fp8_d64.hip", "csa_stream_bf16_d32.hip", "csa_kernels.hip",
+           "csa_sort.hip", "csa_plan.cpp", "csa_abi.cpp"]
 
 ARCH = "gfx950"
 FLAGS = [
@@ -43,7 +46,7 @@ def _compile(src: str) -> str:
 def build() -> str:
     """Compile every source for gfx950 and link libcsa_index.so."""
     os.makedirs(OBJDIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     cmd = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]

@@ -2,8 +2,9 @@
 //
 // Every call validates and plans on the host first (nothing touches the
 // device on an invalid call), then enqueues, on the caller's stream: the
-// scoring kernel (scores + running top-k per query position) and the row
-// sort.  No host synchronisation, no host<->device copies.
+// scoring kernel (scores + running top-k per query position, or per key
+// range), the merge of the key ranges' lists when there are several, and
+// the row sort.  No host synchronisation, no host<->device copies.
 #include <hip/hip_runtime_api.h>
 
 #include <cstdint>
@@ -71,7 +72,7 @@ extern "C" int csa_plan_query(const csa_desc *desc, int32_t m, int32_t k,
     out->chunk_keys = p.chunk;
     out->log_capacity = p.log_cap;
     out->grid = p.grid;
-    out->reserved0 = 0;
+    out->key_splits = p.n_splits;
     out->n_blocks = p.n_blocks;
     out->workspace_bytes = p.ws_bytes;
     return CSA_OK;
@@ -123,6 +124,11 @@ extern "C" int csa_index_ex(const void *q, const float *w, const void *k_cmp,
     a.out_idx = out_idx;
     a.out_score = out_score;
     a.ws = static_cast<uint32_t *>(ws);
+    unsigned char *part = static_cast<unsigned char *>(ws) + p.part_offset;
+    a.part_idx = p.n_splits > 1 ? reinterpret_cast<int32_t *>(part) : nullptr;
+    a.part_score = p.n_splits > 1
+        ? reinterpret_cast<float *>(part + size_t(p.B * p.S) * size_t(p.n_splits) * size_t(p.k) * 4u)
+        : nullptr;
     a.B = p.B;
     a.S = p.S;
     a.T = p.T;
@@ -130,14 +136,20 @@ extern "C" int csa_index_ex(const void *q, const float *w, const void *k_cmp,
     a.m = p.m;
     a.topk = p.k;
     a.log_cap = p.log_cap;
+    a.n_splits = p.n_splits;
+    a.split_keys = p.split_keys;
     a.blocks_per_batch = p.blocks_per_batch;
-    a.n_blocks = p.n_blocks;
+    a.n_units = p.n_units;
 
     rc = CSA_OK;
     if (opt && opt->timing[0] && hipEventRecord(opt->timing[0], stream) != hipSuccess)
         rc = CSA_ERR_HIP;
     if (rc == CSA_OK && csa::launch_stream_topk(p, a, stream) != hipSuccess) rc = CSA_ERR_HIP;
     if (rc == CSA_OK && opt && opt->timing[1] && hipEventRecord(opt->timing[1], stream) != hipSuccess)
+        rc = CSA_ERR_HIP;
+    if (rc == CSA_OK &&
+        csa::launch_merge_splits(p, a.part_idx, a.part_score, out_idx, out_score, cus, stream) !=
+            hipSuccess)
         rc = CSA_ERR_HIP;
     if (rc == CSA_OK && csa::launch_sort_rows(p, out_idx, out_score, cus, stream) != hipSuccess)
         rc = CSA_ERR_HIP;

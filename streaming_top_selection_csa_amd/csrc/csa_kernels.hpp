@@ -19,12 +19,24 @@ struct StreamArgs {
     int32_t *out_idx;           // [B, S, k]
     float *out_score;           // [B, S, k]
     uint32_t *ws;               // candidate logs: grid * 8 waves * QW * log_cap * 8 bytes
+    int32_t *part_idx;          // [B, S, G, k] per-key-range top-k lists (G > 1)
+    float *part_score;          // [B, S, G, k]
     int64_t B, S, T, row_offset;
     int m, topk, log_cap;
-    int64_t blocks_per_batch, n_blocks;
+    int n_splits, split_keys;   // G key ranges of split_keys keys (G = 1: all keys)
+    int64_t blocks_per_batch, n_units;
 };
 
 hipError_t launch_stream_topk(const Plan &p, const StreamArgs &a, hipStream_t s);
+// per operand type and head dimension (csa_stream_*.hip)
+hipError_t launch_stream_bf16_d32(int H, const StreamArgs &a, int grid, hipStream_t s);
+hipError_t launch_stream_bf16_d64(int H, const StreamArgs &a, int grid, hipStream_t s);
+hipError_t launch_stream_bf16_d128(int H, const StreamArgs &a, int grid, hipStream_t s);
+hipError_t launch_stream_fp8_d64(int H, const StreamArgs &a, int grid, hipStream_t s);
+hipError_t launch_stream_fp8_d128(int H, const StreamArgs &a, int grid, hipStream_t s);
+// Top-k of the G partial lists of every position into the (unsorted) rows.
+hipError_t launch_merge_splits(const Plan &p, const int32_t *part_idx, const float *part_score,
+                               int32_t *out_idx, float *out_score, int num_cus, hipStream_t s);
 hipError_t launch_sort_rows(const Plan &p, int32_t *out_idx, float *out_score, int num_cus,
                             hipStream_t s);
 

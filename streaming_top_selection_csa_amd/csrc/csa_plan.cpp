@@ -1,6 +1,8 @@
 // csa_plan.cpp -- argument validation and launch planning (host only).
 #include "csa_plan.hpp"
 
+#include <algorithm>
+
 namespace csa {
 
 bool supported(int dtype, int H, int D)
@@ -38,11 +40,14 @@ int make_plan(const csa_desc *desc, int32_t m, int32_t k,
 
     int64_t row_offset = 0;
     int chunk = 0;
+    int splits_req = 0;
     if (opt) {
         if (opt->row_offset < 0 || opt->chunk_keys < 0 || opt->chunk_keys > kMaxChunk)
             return CSA_ERR_INVALID_ARG;
+        if (opt->key_splits < 0 || opt->reserved1 != 0) return CSA_ERR_INVALID_ARG;
         row_offset = opt->row_offset;
         chunk = opt->chunk_keys;
+        splits_req = opt->key_splits;
     }
     // positions must stay representable: t + 1 fits comfortably in int64
     if (desc->S > (int64_t(1) << 40) || row_offset > (int64_t(1) << 40))
@@ -74,13 +79,36 @@ int make_plan(const csa_desc *desc, int32_t m, int32_t k,
     p.blocks_per_batch = (desc->S + p.QB - 1) / p.QB;
     p.n_blocks = p.blocks_per_batch * desc->B;
     const int64_t resident = int64_t(num_cus);  // one 8-wave workgroup per CU
-    p.grid = int(p.n_blocks < resident ? p.n_blocks : resident);
+
+    // key ranges: requested, or automatic when the query blocks leave CUs idle
+    const int64_t n_max = desc->S > 0 ? std::min<int64_t>(desc->T, (row_offset + desc->S) / m) : 0;
+    const int64_t tiles = (n_max + kKeysPerTile - 1) / kKeysPerTile;
+    int64_t G = 1;
+    if (splits_req > 0) {
+        G = std::min<int64_t>(splits_req, tiles);
+    } else if (p.n_blocks > 0 && p.n_blocks < resident) {
+        const int64_t min_keys = std::max<int64_t>(k, kMinSplitKeys);
+        G = std::min<int64_t>((resident + p.n_blocks - 1) / p.n_blocks, n_max / min_keys);
+    }
+    const int64_t g_cap = int64_t(kMaxSplitBytes / (size_t(rows > 0 ? rows : 1) * size_t(k) * 8u));
+    G = std::max<int64_t>(1, std::min(G, g_cap));
+    if (G > 1) {
+        const int64_t per = (n_max + G - 1) / G;
+        p.split_keys = int((per + kKeysPerTile - 1) / kKeysPerTile * kKeysPerTile);
+        G = (n_max + p.split_keys - 1) / p.split_keys;
+    }
+    p.n_splits = int(G);
+    if (p.n_splits == 1) p.split_keys = 0;
+    p.n_units = p.n_blocks * p.n_splits;
+    p.grid = int(p.n_units < resident ? p.n_units : resident);
     p.chunk = chunk;
     p.log_cap = k + chunk;
     p.sort_pow2 = int(next_pow2(k));
     const size_t per_wave = size_t(p.QW) * size_t(p.log_cap) * 8u;  // u32 key + i32 index
-    size_t ws = size_t(p.grid) * kWaves * per_wave;
-    p.ws_bytes = (ws + 255) / 256 * 256;
+    const size_t logs = (size_t(p.grid) * kWaves * per_wave + 255) / 256 * 256;
+    p.part_offset = logs;
+    const size_t parts = p.n_splits > 1 ? size_t(rows) * size_t(p.n_splits) * size_t(k) * 8u : 0u;
+    p.ws_bytes = logs + (parts + 255) / 256 * 256;
     *plan = p;
     return CSA_OK;
 }

@@ -10,6 +10,13 @@
 // Top-k, Abstract: chunked partition-merge top-k that never materialises the
 // full score tensor).  The workspace therefore depends on the grid, k and
 // the chunk size, never on S or T.
+//
+// When the query blocks are too few to fill the device (a short query block
+// at the end of a long context, a decode step) the visible keys are also
+// split into G ranges of split_keys keys: each (query block, key range) unit
+// produces the exact top-k of its range, and a merge pass selects the top-k
+// of the G partial lists per position.  Only then does the workspace grow,
+// by B*S*G*k candidate entries.
 #pragma once
 
 #include <cstddef>
@@ -25,6 +32,8 @@ constexpr int kRowsPerWave = 64;    // (position, head) rows of q per wave
 constexpr int kKeysPerTile = 64;    // compressed keys per LDS tile
 constexpr int kMaxTopK = 16384;     // row sort holds next_pow2(k) keys in LDS
 constexpr int kMaxChunk = 1 << 20;
+constexpr int kMinSplitKeys = 1024;              // smallest automatic key range
+constexpr size_t kMaxSplitBytes = size_t(1) << 30;  // bound of the partial lists
 
 struct Plan {
     int64_t B = 0, S = 0, T = 0, row_offset = 0;
@@ -32,11 +41,15 @@ struct Plan {
     int QW = 0;                 // positions per wave (64 / H)
     int QB = 0;                 // positions per block (8 * QW)
     int64_t blocks_per_batch = 0;
-    int64_t n_blocks = 0;
+    int64_t n_blocks = 0;       // query blocks over all batch entries
+    int n_splits = 1;           // key ranges per query block (G)
+    int split_keys = 0;         // keys per range (multiple of 64) when G > 1
+    int64_t n_units = 0;        // n_blocks * n_splits scoring units
     int grid = 0;               // scoring workgroups (persistent)
     int chunk = 0;              // candidates buffered beyond k before a merge
     int log_cap = 0;            // k + chunk
     int sort_pow2 = 0;          // next power of two >= k
+    size_t part_offset = 0;     // byte offset of the partial lists (G > 1)
     size_t ws_bytes = 0;        // 256-aligned
 };
 

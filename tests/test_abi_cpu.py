@@ -146,3 +146,40 @@ def test_binding_refuses_host_tensors(lib):
     k = torch.zeros((1, 2, 128), dtype=torch.bfloat16)
     with pytest.raises(TypeError):
         csa.index(q, w, k, 4, 2)
+
+
+def test_key_splits_plan(lib):
+    """Key ranges appear only when the query blocks leave compute units idle,
+    and the workspace then holds B*S*G*k partial entries."""
+    # 64 positions at the end of a 262,144-position context, 65,536 keys
+    dec = csa.make_desc(1, 64, 65536, 64, 128)
+    info = csa.plan_query(dec, 4, 2048, opts(row_offset=4 * 65536 - 64))
+    assert info.n_blocks == 8
+    assert info.key_splits == 32                       # min(256/8, 65536/2048)
+    assert info.grid == 256
+    logs = 256 * 8 * (2048 + 8192) * 8
+    assert info.workspace_bytes == logs + 64 * 32 * 2048 * 8
+    # early positions see few keys: no range below max(k, 1024) keys
+    early = csa.plan_query(dec, 4, 2048, opts(row_offset=0))
+    assert early.key_splits == 1 and early.workspace_bytes == 256 * 8 * (2048 + 8192) * 8 // 32
+    # enough query blocks: never split
+    big = csa.plan_query(csa.make_desc(1, 65536, 16384, 64, 128), 4, 2048, opts())
+    assert big.key_splits == 1
+    # requested ranges: at most one per 64 visible keys
+    assert csa.plan_query(dec, 4, 2048, opts(row_offset=262080, key_splits=5)).key_splits == 5
+    assert csa.plan_query(dec, 4, 2048, opts(row_offset=262080, key_splits=1)).key_splits == 1
+    few = csa.plan_query(csa.make_desc(1, 8, 100, 64, 128), 4, 16, opts(row_offset=1000,
+                                                                        key_splits=50))
+    assert few.key_splits == 2                         # 100 keys -> 2 tiles
+    # the partial lists stay under 1 GiB: G is lowered
+    wide = csa.plan_query(csa.make_desc(1, 2048, 65536, 64, 128), 4, 16384,
+                          opts(row_offset=262144, key_splits=64))
+    assert 2048 * wide.key_splits * 16384 * 8 <= 1 << 30
+
+
+def test_key_splits_validation(lib):
+    ok = csa.make_desc(1, 100, 25, 64, 128)
+    assert bad(lib, ok, opt=opts(key_splits=-1)) == B.CSA_ERR_INVALID_ARG
+    o = opts()
+    o.reserved1 = 3
+    assert bad(lib, ok, opt=o) == B.CSA_ERR_INVALID_ARG
