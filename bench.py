@@ -34,7 +34,7 @@ if ROOT not in sys.path:
 
 METRIC = "indexer queries/sec + MFMA TFLOP/s (% peak) + peak HBM GB at S=262K, 1 GPU"
 PEAK_TFLOPS = {"bf16": 2500.0, "e4m3fn": 5000.0}   # MI355X dense MFMA
-KERNEL_SRC = os.path.join(ROOT, "streaming_top_selection_csa_amd", "csrc", "csa_kernels.hip")
+KERNEL_SRC = os.path.join(ROOT, "streaming_top_selection_csa_amd", "csrc", "csa_stream.hpp")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "stream_topk_s256k_pmc.md")
 
 
