@@ -14,12 +14,14 @@ constexpr int kMergeThreads = 512;
 constexpr int kMergeWaves = kMergeThreads / 64;
 constexpr int kMergeBins = 4096;  // top 12 bits of the order key
 constexpr int kMergeCap = 6144;   // candidates of the k-th bin held in LDS
+constexpr int kMergeEpt = 8;      // consecutive list entries per thread in the gather
 
 struct MergeShared {
     uint32_t hist[kMergeBins];
     uint32_t cu[kMergeCap];
     int32_t ci[kMergeCap];
     uint32_t w[kMergeWaves];
+    uint32_t w2[2][kMergeWaves];
     uint32_t sel[2];
     int first;
     int out;
@@ -120,8 +122,17 @@ merge_splits_kernel(const int32_t *__restrict__ pidx, const float *__restrict__ 
             sh.out = 0;
         }
         __syncthreads();
-        for (int e = tid; e < n; e += kMergeThreads)
-            atomicAdd(&sh.hist[order_key(rs[e]) >> 20], 1u);
+        for (int base = 0; base < n; base += 4 * kMergeThreads) {
+            uint32_t bin[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int e = base + j * kMergeThreads + tid;
+                bin[j] = e < n ? order_key(rs[e]) >> 20 : uint32_t(kMergeBins);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (bin[j] < uint32_t(kMergeBins)) atomicAdd(&sh.hist[bin[j]], 1u);
+        }
         __syncthreads();
 
         // ---- the bin of the k-th best: thread t owns the PER bins just below
@@ -167,30 +178,54 @@ merge_splits_kernel(const int32_t *__restrict__ pidx, const float *__restrict__ 
         int need = k - n_above;                  // still to take, >= 1
         const bool fast = in_bin <= kMergeCap;
         if (fast) {
-            // ---- higher bins to the row, the k-th bin into LDS in list order
+            // ---- higher bins to the row, the k-th bin into LDS in list order:
+            // thread t takes entries [base + t*EPT, base + (t+1)*EPT), so a
+            // scan of the per-thread candidate counts places them in order
             int cpos = 0;
-            for (int base = 0; base < n; base += kMergeThreads) {
-                const int e = base + tid;
-                float sc = 0.f;
-                uint32_t u = 0u;
-                if (e < n) {
-                    sc = rs[e];
-                    u = order_key(sc);
+            int step = 0;
+            for (int base = 0; base < n; base += kMergeThreads * kMergeEpt, ++step) {
+                const int e0 = base + tid * kMergeEpt;
+                float sc[kMergeEpt];
+                uint32_t u[kMergeEpt];
+                int nc = 0;
+#pragma unroll
+                for (int j = 0; j < kMergeEpt; ++j) {
+                    const bool valid = e0 + j < n;
+                    sc[j] = valid ? rs[e0 + j] : 0.f;
+                    u[j] = valid ? order_key(sc[j]) : 0u;
                 }
-                const uint32_t bin = u >> 20;
-                if (e < n && bin > bstar) {
-                    const int p = atomicAdd(&sh.out, 1);
-                    if (p < n_above) {
-                        oi[p] = ri[e];
-                        os[p] = sc;
+#pragma unroll
+                for (int j = 0; j < kMergeEpt; ++j) {
+                    const bool valid = e0 + j < n;
+                    const uint32_t bin = u[j] >> 20;
+                    if (valid && bin > bstar) {
+                        const int p = atomicAdd(&sh.out, 1);
+                        if (p < n_above) {
+                            oi[p] = ri[e0 + j];
+                            os[p] = sc[j];
+                        }
                     }
+                    nc += (valid && bin == bstar) ? 1 : 0;
                 }
-                const bool cand = e < n && bin == bstar;
-                int tot;
-                const int r = block_rank(cand, sh.w, lane, wave, &tot);
-                if (cand) {
-                    sh.cu[cpos + r] = u;
-                    sh.ci[cpos + r] = ri[e];
+                const uint32_t incl = wave_prefix_sum(uint32_t(nc));
+                uint32_t *w2 = sh.w2[step & 1];  // alternate: one barrier per step
+                if (lane == 63) w2[wave] = incl;
+                __syncthreads();
+                int wbase = 0, tot = 0;
+#pragma unroll
+                for (int v = 0; v < kMergeWaves; ++v) {
+                    const int c2 = int(w2[v]);
+                    wbase += v < wave ? c2 : 0;
+                    tot += c2;
+                }
+                int pos = cpos + wbase + int(incl) - nc;
+#pragma unroll
+                for (int j = 0; j < kMergeEpt; ++j) {
+                    if (e0 + j < n && (u[j] >> 20) == bstar) {
+                        sh.cu[pos] = u[j];
+                        sh.ci[pos] = ri[e0 + j];
+                        ++pos;
+                    }
                 }
                 cpos += tot;
             }

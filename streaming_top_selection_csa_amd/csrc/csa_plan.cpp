@@ -87,7 +87,9 @@ int make_plan(const csa_desc *desc, int32_t m, int32_t k,
     if (splits_req > 0) {
         G = std::min<int64_t>(splits_req, tiles);
     } else if (p.n_blocks > 0 && p.n_blocks < resident) {
-        const int64_t min_keys = std::max<int64_t>(k, kMinSplitKeys);
+        // a range of at least 2k keys: the merge reads G*k entries per
+        // position, the scoring of a unit takes keys/G
+        const int64_t min_keys = std::max<int64_t>(int64_t(2) * k, kMinSplitKeys);
         G = std::min<int64_t>((resident + p.n_blocks - 1) / p.n_blocks, n_max / min_keys);
     }
     const int64_t g_cap = int64_t(kMaxSplitBytes / (size_t(rows > 0 ? rows : 1) * size_t(k) * 8u));

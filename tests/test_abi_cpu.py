@@ -155,11 +155,11 @@ def test_key_splits_plan(lib):
     dec = csa.make_desc(1, 64, 65536, 64, 128)
     info = csa.plan_query(dec, 4, 2048, opts(row_offset=4 * 65536 - 64))
     assert info.n_blocks == 8
-    assert info.key_splits == 32                       # min(256/8, 65536/2048)
-    assert info.grid == 256
-    logs = 256 * 8 * (2048 + 8192) * 8
-    assert info.workspace_bytes == logs + 64 * 32 * 2048 * 8
-    # early positions see few keys: no range below max(k, 1024) keys
+    assert info.key_splits == 16                       # min(256/8, 65536/(2*2048))
+    assert info.grid == 8 * 16
+    logs = 8 * 16 * 8 * (2048 + 8192) * 8
+    assert info.workspace_bytes == logs + 64 * 16 * 2048 * 8
+    # early positions see few keys: no range below max(2k, 1024) keys
     early = csa.plan_query(dec, 4, 2048, opts(row_offset=0))
     assert early.key_splits == 1 and early.workspace_bytes == 256 * 8 * (2048 + 8192) * 8 // 32
     # enough query blocks: never split
