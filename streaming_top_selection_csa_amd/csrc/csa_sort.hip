@@ -62,11 +62,81 @@ sort_rows_kernel(int32_t *out_idx, float *out_score, int64_t nrows, int k, int p
 // slots l*E .. l*E+E-1 as 64-bit keys in registers; a bitonic network runs
 // its stages of stride < E inside each lane and the others across lanes
 // with shuffles, with no workgroup barrier.
+// The value of lane (lane ^ D) for D = 1, 2, ..., 32, by lane permutes
+// that stay in registers: DPP quad permutes (1, 2), a bit-mask swizzle
+// inside each half-wave (4), a DPP rotation by half a 16-lane row (8), and
+// the row-pair and half-wave swaps (16, 32), which give every lane both the
+// lower and the upper lane's value.
+template <int D>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v, int lane)
+{
+    if constexpr (D == 1) {
+        return __builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xf, 0xf, false);  // quad_perm 1,0,3,2
+    } else if constexpr (D == 2) {
+        return __builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xf, 0xf, false);  // quad_perm 2,3,0,1
+    } else if constexpr (D == 4) {
+        return uint32_t(__builtin_amdgcn_ds_swizzle(int(v), 0x101F));      // and 31, xor 4
+    } else if constexpr (D == 8) {
+        return __builtin_amdgcn_update_dpp(0u, v, 0x128, 0xf, 0xf, false); // row_ror:8
+    } else if constexpr (D == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (lane & 16) ? r[0] : r[1];
+    } else {
+        static_assert(D == 32, "partner lane distance");
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (lane & 32) ? r[0] : r[1];
+    }
+}
+
+// One compare-exchange step of the bitonic network over N = 64*E keys held
+// E per lane in blocked order (lane l holds positions l*E .. l*E+E-1):
+// merging runs of SIZE, partners STRIDE positions apart.  Ascending order.
+template <int E, int SIZE, int STRIDE>
+__device__ __forceinline__ void bitonic_step(unsigned long long (&key)[E], int lane)
+{
+    if constexpr (STRIDE < E) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int f = e ^ STRIDE;
+            if (f > e) {
+                const bool up = ((lane * E + e) & SIZE) == 0;
+                const unsigned long long x = key[e], y = key[f];
+                const bool sw = (x > y) == up;
+                key[e] = sw ? y : x;
+                key[f] = sw ? x : y;
+            }
+        }
+    } else {
+        constexpr int D = STRIDE / E;  // partner lane distance
+        const bool lower = (lane & D) == 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const unsigned long long o =
+                (static_cast<unsigned long long>(lane_xor<D>(uint32_t(key[e] >> 32), lane)) << 32) |
+                lane_xor<D>(uint32_t(key[e]), lane);
+            const bool up = ((lane * E + e) & SIZE) == 0;
+            const bool keep_min = lower == up;
+            const unsigned long long mn = key[e] < o ? key[e] : o;
+            const unsigned long long mx = key[e] < o ? o : key[e];
+            key[e] = keep_min ? mn : mx;
+        }
+    }
+    if constexpr (STRIDE > 1) bitonic_step<E, SIZE, STRIDE / 2>(key, lane);
+}
+
+template <int E, int SIZE>
+__device__ __forceinline__ void bitonic_sort(unsigned long long (&key)[E], int lane)
+{
+    bitonic_step<E, SIZE, SIZE / 2>(key, lane);
+    if constexpr (SIZE < 64 * E) bitonic_sort<E, SIZE * 2>(key, lane);
+}
+
+// One wave per row: next_pow2(k) = 64*E keys (score desc, index asc as the
+// ascending 64-bit key ~orderkey(score) << 32 | index), padding as all-ones.
 template <int E>
 __global__ void __launch_bounds__(256)
 sort_rows_wave_kernel(int32_t *out_idx, float *out_score, int64_t nrows, int k)
 {
-    constexpr int N = 64 * E;
     const int lane = threadIdx.x & 63;
     const int64_t wave = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
     const int64_t nwaves = int64_t(gridDim.x) * 4;
@@ -82,37 +152,7 @@ sort_rows_wave_kernel(int32_t *out_idx, float *out_score, int64_t nrows, int k)
                 key[e] = (static_cast<unsigned long long>(~order_key(rs[pos])) << 32) |
                          uint32_t(ri[pos]);
         }
-#pragma unroll
-        for (int size = 2; size <= N; size <<= 1) {
-#pragma unroll
-            for (int stride = size >> 1; stride > 0; stride >>= 1) {
-                if (stride < E) {
-#pragma unroll
-                    for (int e = 0; e < E; ++e) {
-                        const int f = e ^ stride;
-                        if (f > e) {
-                            const bool up = ((lane * E + e) & size) == 0;
-                            const unsigned long long x = key[e], y = key[f];
-                            const bool sw = (x > y) == up;
-                            key[e] = sw ? y : x;
-                            key[f] = sw ? x : y;
-                        }
-                    }
-                } else {
-                    const int d = stride / E;  // partner lane distance
-                    const bool lower = (lane & d) == 0;
-#pragma unroll
-                    for (int e = 0; e < E; ++e) {
-                        const unsigned long long o = __shfl_xor(key[e], d);
-                        const bool up = ((lane * E + e) & size) == 0;
-                        const bool keep_min = lower == up;
-                        const unsigned long long mn = key[e] < o ? key[e] : o;
-                        const unsigned long long mx = key[e] < o ? o : key[e];
-                        key[e] = keep_min ? mn : mx;
-                    }
-                }
-            }
-        }
+        bitonic_sort<E, 2>(key, lane);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             const int pos = lane * E + e;
