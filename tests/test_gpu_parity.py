@@ -68,6 +68,8 @@ SMALL_EXACT = [
     (1, 100, 1, 1, 32, 7, -1),
     (1, 90, 1, 64, 128, 5, 40),      # T smaller than S/m: every late row sees all keys
     (1, 3000, 4, 64, 128, 2048, -1),  # k larger than most visible sets
+    (1, 14000, 4, 64, 128, 3000, -1),  # rows wider than 2048: workgroup row sort in LDS
+    (1, 21000, 4, 64, 128, 5000, -1),  # same, 8192-key rows
 ]
 
 
