@@ -708,7 +708,9 @@ stream_topk_kernel(StreamArgs a)
     constexpr int PD = NBUF - 1;                     // tiles loaded ahead
     constexpr int NB = 512 / QW;                     // threshold bins per position
     constexpr int HEAD = NB / 8 > 1 ? NB / 8 : 1;    // headroom above the max seen
-    constexpr int UPD = 64;                          // appends between refreshes
+    // appends between threshold refreshes: a refresh costs two LDS round
+    // trips and a wave scan, a looser threshold only some extra appends
+    constexpr int UPD = 512;
 
     __shared__ __attribute__((aligned(16))) unsigned char s_k[NBUF][TILEB];
     __shared__ float s_ks[NBUF][KT];
