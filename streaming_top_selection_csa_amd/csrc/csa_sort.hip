@@ -133,34 +133,72 @@ __device__ __forceinline__ void bitonic_sort(unsigned long long (&key)[E], int l
 
 // One wave per row: next_pow2(k) = 64*E keys (score desc, index asc as the
 // ascending 64-bit key ~orderkey(score) << 32 | index), padding as all-ones.
+// Rows move between memory and the blocked register layout through a
+// per-wave LDS buffer, one 32-bit half at a time: the global loads and
+// stores then cover whole cache lines (consecutive lanes, consecutive
+// elements), and the buffer's one-word pad per 32 keeps each lane's run of
+// E words on distinct banks.
 template <int E>
 __global__ void __launch_bounds__(256)
 sort_rows_wave_kernel(int32_t *out_idx, float *out_score, int64_t nrows, int k)
 {
+    constexpr int N = 64 * E;
+    constexpr int NPAD = N + N / 32;
+    __shared__ uint32_t s_buf[4][NPAD];
     const int lane = threadIdx.x & 63;
-    const int64_t wave = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    const int w = threadIdx.x >> 6;
+    uint32_t *sb = s_buf[w];
+    const int64_t wave = int64_t(blockIdx.x) * 4 + w;
     const int64_t nwaves = int64_t(gridDim.x) * 4;
+    auto pad = [](int i) { return i + (i >> 5); };
+    auto lds_sync = [] {
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_wave_barrier();
+    };
     for (int64_t row = wave; row < nrows; row += nwaves) {
         int32_t *ri = out_idx + row * k;
         float *rs = out_score + row * k;
         unsigned long long key[E];
+        // high halves: ~orderkey(score), all-ones past k
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const int pos = lane * E + e;
-            key[e] = ~0ull;
-            if (pos < k)
-                key[e] = (static_cast<unsigned long long>(~order_key(rs[pos])) << 32) |
-                         uint32_t(ri[pos]);
+        for (int j = 0; j < E; ++j) {
+            const int i = j * 64 + lane;
+            sb[pad(i)] = i < k ? ~order_key(rs[i]) : 0xFFFFFFFFu;
         }
+        lds_sync();
+#pragma unroll
+        for (int e = 0; e < E; ++e) key[e] = static_cast<unsigned long long>(sb[pad(lane * E + e)]) << 32;
+        lds_sync();
+        // low halves: the key index
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+            const int i = j * 64 + lane;
+            sb[pad(i)] = i < k ? uint32_t(ri[i]) : 0xFFFFFFFFu;
+        }
+        lds_sync();
+#pragma unroll
+        for (int e = 0; e < E; ++e) key[e] |= sb[pad(lane * E + e)];
         bitonic_sort<E, 2>(key, lane);
+        lds_sync();
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const int pos = lane * E + e;
-            if (pos < k) {
-                ri[pos] = int32_t(uint32_t(key[e]));
-                rs[pos] = key_to_float(~uint32_t(key[e] >> 32));
-            }
+        for (int e = 0; e < E; ++e) sb[pad(lane * E + e)] = uint32_t(key[e]);
+        lds_sync();
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+            const int i = j * 64 + lane;
+            if (i < k) ri[i] = int32_t(sb[pad(i)]);
         }
+        lds_sync();
+#pragma unroll
+        for (int e = 0; e < E; ++e) sb[pad(lane * E + e)] = uint32_t(key[e] >> 32);
+        lds_sync();
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+            const int i = j * 64 + lane;
+            if (i < k) rs[i] = key_to_float(~sb[pad(i)]);
+        }
+        lds_sync();
     }
 }
 
