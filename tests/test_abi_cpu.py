@@ -183,3 +183,16 @@ def test_key_splits_validation(lib):
     o = opts()
     o.reserved1 = 3
     assert bad(lib, ok, opt=o) == B.CSA_ERR_INVALID_ARG
+
+
+def test_bench_visible_pairs_closed_form():
+    """bench.py's closed-form count of visible (position, key) pairs against
+    the direct sum over positions."""
+    import bench
+    for S, T, m, off in [(1024, 256, 4, 0), (1000, 250, 4, 0), (777, 300, 3, 0), (90, 40, 1, 0),
+                         (64, 65536, 4, 4 * 65536 - 64), (300, 50, 2, 17), (5, 0, 4, 0),
+                         (4096, 2000, 4, 100)]:
+        direct = sum(min(T, (t + 1) // m) for t in range(off, off + S))
+        assert bench.visible_pairs(S, T, m, 1, off) == direct, (S, T, m, off)
+    # the headline shape: m*T*(T-1)/2 + T with S = m*T
+    assert bench.visible_pairs(262144, 65536, 4) == 4 * 65536 * 65535 // 2 + 65536
