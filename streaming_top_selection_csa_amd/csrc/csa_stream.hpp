@@ -975,9 +975,9 @@ stream_topk_kernel(StreamArgs a)
             float ksv = 1.f;
             if constexpr (FP8) ksv = s_ks[buf][lane];
             // Each wave stages its share of tile it+PD (over tile it-1, which
-            // every wave has finished) right after its own filter step: the
-            // LDS writes of a filter step wait for this wave's outstanding
-            // loads, and these are then always at least an iteration old.
+            // every wave has finished) after its own filter step, so that the
+            // leading and the lagging waves issue their loads half a tile
+            // apart.
             const bool stage = it + PD < ntiles;
             if (!lagging) {
                 mma_half(buf, 0);
