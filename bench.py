@@ -170,7 +170,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build measures one GPU only (the indexer path is single-GPU); "
+        print("bench.py: measures one GPU only (the indexer path is single-GPU); "
               "run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
