@@ -5,8 +5,8 @@ the indexer's arithmetic (no scoring, no selection).  Both the HIP path and
 the CPU oracle consume the tensors it produces, bit for bit.
 
 The workloads are V4-shaped indexer inputs (StreamIndex: Memory-Bounded
-Compressed Sparse Attention via Streaming Top-k, Abstract: synthetic inputs
-with H_I = 64 indexer heads and compression ratio m = 4 at the indexer step).
+Compressed Sparse Attention via Streaming Top-k, Abstract: synthetic inputs;
+the indexer has H_I = 64 heads and the keys are compressed by m = 4).
 The distributions below are the ones the benchmark configurations name:
 
 * ``int``   : q and k integers uniform in [-3, 3], w integers uniform in

@@ -2,9 +2,9 @@
  * csa_index.h -- C ABI of the MI355X (gfx950) CSA lightning-indexer top-k.
  *
  * Operation (StreamIndex: Memory-Bounded Compressed Sparse Attention via
- * Streaming Top-k, Abstract): a lightning indexer scores the compressed keys
- * for every query position and the top-k keys are selected per query, without
- * ever materialising the [B, S, H_I, T] score tensor.  For query position t
+ * Streaming Top-k, Abstract): each query position rates every compressed key
+ * with the lightning indexer and keeps its k best keys; the [B, S, H_I, T]
+ * tensor of per-head scores is never formed.  For query position t
  * (batch entry b) and compressed key s the score is
  *
  *     I(t, s) = sum_{j < H} w[b,t,j] * max(0, q[b,t,j,:] . k_cmp[b,s,:])

@@ -7,8 +7,8 @@
  * definition that the GPU path is checked against.
  *
  * What it computes (StreamIndex: Memory-Bounded Compressed Sparse Attention
- * via Streaming Top-k, Abstract): the lightning indexer scores compressed keys
- * for each query and the top-k keys are selected per query.  The scoring rule
+ * via Streaming Top-k, Abstract): every query position rates each compressed key
+ * with the lightning indexer and keeps its k best keys.  The scoring rule
  * used throughout is
  *
  *     I(t, s) = sum_j  w[t, j] * max(0, q[t, j, :] . k[s, :])

@@ -7,8 +7,8 @@
 // positions in ascending order, 64 keys per staged tile, and keeps a running
 // top-k per position in a bounded candidate log of k + chunk entries
 // (StreamIndex: Memory-Bounded Compressed Sparse Attention via Streaming
-// Top-k, Abstract: chunked partition-merge top-k that never materialises the
-// full score tensor).  The workspace therefore depends on the grid, k and
+// Top-k, Abstract: the keys are taken in chunks and each chunk's winners are
+// merged into the running set, so the full score tensor is never formed).  The workspace therefore depends on the grid, k and
 // the chunk size, never on S or T.
 //
 // When the query blocks are too few to fill the device (a short query block

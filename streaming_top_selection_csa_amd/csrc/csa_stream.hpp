@@ -3,9 +3,9 @@
 // per operand type and head dimension, and by csa_kernels.hip).
 //
 // StreamIndex: Memory-Bounded Compressed Sparse Attention via Streaming
-// Top-k (Abstract) computes, per query position, lightning-indexer scores
-// over the compressed keys and keeps the top-k, with a chunked
-// partition-merge driver that never materialises the [B,S,H_I,T] tensor.
+// Top-k (Abstract): each query position rates the compressed keys with the
+// lightning indexer and keeps its k best, folding the keys in chunk by chunk
+// so that no [B,S,H_I,T] tensor is ever formed.
 // Here that is one persistent kernel:
 //
 //   stream_topk_kernel  Each wave owns 64 (position, head) rows of q, held in

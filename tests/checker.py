@@ -1,8 +1,8 @@
 """Comparison of GPU top-k rows against the CPU oracle (test infrastructure).
 
 Acceptance, per the indexer's definition (StreamIndex: Memory-Bounded
-Compressed Sparse Attention via Streaming Top-k, Abstract: top-k per query;
-set-overlap recall against the exact ground truth):
+Compressed Sparse Attention via Streaming Top-k, Abstract: the k best keys
+of each query, judged by how much of the exact top-k set is recovered):
 
 * exact inputs (integer-valued, every fp32 partial sum exact): indices and
   scores identical to the oracle, element by element;

@@ -5,8 +5,8 @@ rational brute force (a different selection algorithm: k rounds of argmax),
 a hand-derived worked example, a library routine (numpy matmul + lexsort,
 torch's bf16 / e4m3fn casts), closed forms and invariants of the
 definition (StreamIndex: Memory-Bounded Compressed Sparse Attention via
-Streaming Top-k, Abstract: lightning-indexer scores, per-query top-k, the
-chunked partition-merge that must reproduce the full result exactly).
+Streaming Top-k, Abstract: lightning-indexer scores, the k best keys of each
+query, and a chunk-by-chunk merge whose result equals the one-shot top-k).
 """
 import json
 import math
