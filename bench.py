@@ -158,7 +158,7 @@ def main():
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--key-splits", type=int, default=0,
                     help="key ranges per query block (0 = automatic, 1 = none)")
-    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="time the five chunk sizes (k=2048) and the five top-k values "
