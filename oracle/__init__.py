@@ -1,17 +1,22 @@
-"""Plain CPU oracle for the CSA lightning-indexer top-k step.
+"""Plain CPU oracle for the CSA lightning-indexer top-k step and the sparse
+attention over the selected keys.
 
 TEST INFRASTRUCTURE ONLY: tests, the smoke check and the benchmark's CPU
 baseline may use this package; the product path never does.  It shares no
 code with the HIP library.
 
-The arithmetic lives in ``csa_oracle.c`` (plain C, double precision); this
-module only builds it with gcc and marshals numpy arrays through ctypes.
+The arithmetic lives in ``csa_oracle.c`` and ``csa_attn_oracle.c`` (plain C,
+double precision); this module only builds them with gcc and marshals numpy
+arrays through ctypes.
 
-Definition followed (StreamIndex: Memory-Bounded Compressed Sparse Attention
+Definitions followed (StreamIndex: Memory-Bounded Compressed Sparse Attention
 via Streaming Top-k, Abstract -- lightning indexer over compressed keys, top-k
 per query): score(t, s) = sum_j w[t,j] * max(0, q[t,j,:] . k[s,:]) for the
 visible keys s < min(T, floor((t+1)/m)); output the first min(k, n_vis) keys
-by (score desc, index asc), padded with index -1 / score -inf.
+by (score desc, index asc), padded with index -1 / score -inf.  Sparse
+attention (same page and section: an attention kernel reads only the chosen
+keys; no formula given): softmax(scale * q[t,h,:] . k[s,:]) over the valid
+entries s of row t's index list, applied to v[s,:].
 """
 from __future__ import annotations
 
@@ -22,7 +27,7 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "csa_oracle.c")
+_SRCS = [os.path.join(_HERE, "csa_oracle.c"), os.path.join(_HERE, "csa_attn_oracle.c")]
 _LIB_PATH = os.path.join(_HERE, "libcsa_oracle.so")
 
 DTYPE_CODES = {"bf16": 0, "e4m3fn": 1, "f32": 2}
@@ -38,7 +43,7 @@ def build(force: bool = True) -> str:
         tmp = _LIB_PATH + ".tmp"
         subprocess.run(
             ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC",
-             "-o", tmp, _SRC, "-lpthread", "-lm"],
+             "-o", tmp, *_SRCS, "-lpthread", "-lm"],
             check=True)
         os.replace(tmp, _LIB_PATH)
         _lib = None
@@ -67,6 +72,9 @@ def _load():
     lib.csa_oracle_decode_e4m3fn.restype = ctypes.c_double
     lib.csa_oracle_n_visible.argtypes = [i64, i64, i32]
     lib.csa_oracle_n_visible.restype = i64
+    lib.csa_oracle_sparse_attention.argtypes = [p, p, p, p, i64, i64, i32, i32, i32,
+                                                ctypes.c_double, i32, p, p, p]
+    lib.csa_oracle_sparse_attention.restype = i32
     _lib = lib
     return lib
 
@@ -149,3 +157,36 @@ def score_pairs(q_rows, w_rows, k_keys, row, key, *, dtype="bf16",
     if rc != 0:
         raise RuntimeError("csa_oracle_score_pairs failed")
     return out
+
+
+def sparse_attention(q_rows, k_keys, v_keys, idx_rows, scale, *, nthreads=None,
+                     with_bound=True):
+    """Softmax attention of each query row over its selected compressed keys.
+
+    q_rows: [n, H, D] bf16 bits (uint16) of the requested rows; k_keys,
+    v_keys: [T, D] bf16 bits; idx_rows: [n, L] int32 index lists, entries
+    outside [0, T) are padding.  Returns (o float64 [n, H, D], lse float64
+    [n, H], a float64 [n, H, D] or None), where a is the softmax-weighted
+    magnitude sum_e p_e |v_e| that bounds rounding in the weights.
+    """
+    lib = _load()
+    q_rows, qp = _arr(q_rows, np.uint16)
+    k_keys, kp = _arr(k_keys, np.uint16)
+    v_keys, vp = _arr(v_keys, np.uint16)
+    idx_rows, ip = _arr(idx_rows, np.int32)
+    n, H, D = q_rows.shape
+    T = k_keys.shape[0]
+    assert v_keys.shape == (T, D) and k_keys.shape[1] == D and idx_rows.shape[0] == n
+    L = idx_rows.shape[1]
+    o = np.empty((n, H, D), np.float64)
+    lse = np.empty((n, H), np.float64)
+    a = np.empty((n, H, D), np.float64) if with_bound else None
+    if nthreads is None:
+        nthreads = min(16, os.cpu_count() or 1)
+    rc = lib.csa_oracle_sparse_attention(
+        qp, kp, vp, ip, n, T, H, D, L, float(scale), int(nthreads),
+        o.ctypes.data_as(ctypes.c_void_p), lse.ctypes.data_as(ctypes.c_void_p),
+        a.ctypes.data_as(ctypes.c_void_p) if a is not None else None)
+    if rc != 0:
+        raise RuntimeError("csa_oracle_sparse_attention failed")
+    return o, lse, a
