@@ -2,6 +2,11 @@
 
     python bench.py [--steps K] [--warmup W] [--workload s256k] [--no-cpu-baseline]
     python bench.py --sweep        chunk-size and top-k sweeps at S=65,536
+    python bench.py --workload attn-s256k [--composite]
+                                   sparse attention over 2,048 selected keys per
+                                   row at S=262,144 (seeded lists, or with
+                                   --composite the indexer's own lists: one step
+                                   is then csa_index followed by the attention)
 
 A step is one csa_index call over the whole workload: scoring of every
 causally visible (query, compressed key) pair on the matrix cores, the
@@ -102,6 +107,123 @@ def cpu_baseline(inp, wl, nrows, seed=0):
                        f"fp64 scores + full sort, {dt:.1f} s")}
 
 
+ATTN_METRIC = "sparse attention over the selected keys, queries/sec at S=262K, 1 GPU"
+COMPOSITE_METRIC = "indexer + sparse attention step, queries/sec at S=262K, 1 GPU"
+INDEXER_FOR = {"attn-s256k": "s256k", "attn-s64k": "s64k"}
+
+
+def attn_cpu_baseline(att, aw, nrows, seed=0):
+    import numpy as np
+
+    import oracle
+    from csa_synth import storage_numpy
+
+    rng = np.random.default_rng(seed)
+    rows = np.sort(rng.choice(aw.S, size=min(nrows, aw.S), replace=False)).astype(np.int64)
+    rt = __import__("torch").as_tensor(rows, device=att["q"].device)
+    q = storage_numpy(att["q"][0].index_select(0, rt))
+    k = storage_numpy(att["k"][0])
+    v = storage_numpy(att["v"][0])
+    idx = att["idx"][0].index_select(0, rt).cpu().numpy()
+    threads = min(len(rows), int(os.environ.get("OMP_NUM_THREADS", "0")) or (os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    oracle.sparse_attention(q, k, v, idx, aw.softmax_scale, nthreads=threads, with_bound=False)
+    dt = time.perf_counter() - t0
+    return {"value": len(rows) / dt, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} seeded uniform rows of {aw.name}, fp64, {dt:.1f} s"}
+
+
+def attention(csa, args):
+    """Sparse attention at an attention shape; with --composite each step is
+    the indexer at the matching shape followed by the attention over its
+    lists.  The attention kernel is timed with HIP events on its stream."""
+    import torch
+    from csa_synth import ATTN_WORKLOADS, WORKLOADS, make_attn_inputs, make_inputs
+
+    aw = ATTN_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    stream = torch.cuda.current_stream(dev)
+    att = make_attn_inputs(aw, seed=0, device=dev)
+    cpu = None
+    if not args.no_cpu_baseline and not args.composite:
+        cpu = attn_cpu_baseline(att, aw, args.cpu_rows // 4)
+    ind = None
+    if args.composite:
+        wl = WORKLOADS[INDEXER_FOR[aw.name]]
+        assert (wl.B, wl.S, wl.n_keys, wl.m, wl.k) == (aw.B, aw.S, aw.T, aw.m, aw.n_sel)
+        del att["idx"]  # the indexer's lists replace the seeded ones
+        ind = make_inputs(wl, seed=0, device=dev)
+        idx = torch.empty((wl.B, wl.S, wl.k), dtype=torch.int32, device=dev)
+        score = torch.empty((wl.B, wl.S, wl.k), dtype=torch.float32, device=dev)
+        ws = csa.workspace_for(ind["q"], ind["k"], wl.m, wl.k)
+    else:
+        idx = att["idx"]
+    out = torch.empty((aw.B, aw.S, aw.H, aw.D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((aw.B, aw.S, aw.H), dtype=torch.float32, device=dev)
+    events = csa.HipEvents(args.steps)
+
+    def step(i=None):
+        if ind is not None:
+            csa.index(ind["q"], ind["w"], ind["k"], wl.m, wl.k, out_idx=idx, out_score=score,
+                      workspace=ws, stream=stream)
+        if i is not None:
+            events.record(events.pairs[i][0], stream)
+        csa.sparse_attention(att["q"], att["k"], att["v"], idx, aw.softmax_scale, out=out,
+                             lse=lse, stream=stream)
+        if i is not None:
+            events.record(events.pairs[i][1], stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kernel_ms = [events.elapsed_ms(i) for i in range(args.steps)]
+    events.close()
+    peak_hbm = torch.cuda.max_memory_allocated(dev)
+
+    entries = int(((idx >= 0) & (idx < aw.T)).sum())       # attended (row, entry) pairs
+    flops = 4.0 * aw.H * aw.D * entries                     # q.k and p.v per head
+    kernel_avg = sum(kernel_ms) / len(kernel_ms)
+    achieved = flops / (kernel_avg * 1e-3) / 1e12
+    gathered = entries * 2 * aw.D * 2                        # one key and one value row each
+    io = (att["q"].numel() + out.numel() + att["k"].numel() + att["v"].numel()) * 2 + \
+        idx.numel() * 4 + lse.numel() * 4
+    ms_per_step = 1e3 * elapsed / args.steps
+    line = {
+        "metric": COMPOSITE_METRIC if ind is not None else ATTN_METRIC,
+        "value": aw.B * aw.S * args.steps / elapsed,
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": aw.name, "B": aw.B, "S": aw.S, "T": aw.T, "H": aw.H, "D": aw.D,
+                   "n_sel": aw.n_sel, "m": aw.m, "lists": "indexer" if ind is not None else
+                   "seeded", "scale": aw.softmax_scale},
+        "attention_kernel_ms": kernel_avg,
+        "attended_entries": entries,
+        "gathered_gb_per_s": gathered / (kernel_avg * 1e-3) / 1e9,
+        "peak_hbm_gb": peak_hbm / 1e9,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS["bf16"],
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_TFLOPS["bf16"],
+                     "traffic": None, "algorithmic_io_gb": io / 1e9,
+                     "gathered_gb": gathered / 1e9},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
 def sweep(csa, args):
     """Chunk-size and top-k sweeps on the S=65,536 workload.  Each cell is
     `warmup` untimed calls and `steps` timed ones on resident inputs."""
@@ -164,6 +286,9 @@ def main():
                     help="time the five chunk sizes (k=2048) and the five top-k values "
                          "(default chunk) on the S=65,536 workload, one JSON line per cell; "
                          "the GPU tests check every cell against the oracle")
+    ap.add_argument("--composite", action="store_true",
+                    help="with an attn-* workload: run the indexer before the attention "
+                         "each step and attend over its lists")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (5 times), to scale "
                          "the HBM byte counters of a profiler run")
@@ -194,6 +319,9 @@ def main():
     csa.load_library()
     if args.sweep:
         sweep(csa, args)
+        return
+    if args.workload.startswith("attn-"):
+        attention(csa, args)
         return
     wl = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")

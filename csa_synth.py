@@ -1,7 +1,9 @@
-"""Seeded synthetic inputs for the CSA lightning-indexer step.
+"""Seeded synthetic inputs for the CSA lightning-indexer step and for the
+sparse attention over the selected keys.
 
 This module only draws random numbers and lays them out; it holds none of
-the indexer's arithmetic (no scoring, no selection).  Both the HIP path and
+the indexer's or the attention's arithmetic (no scoring, no selection, no
+softmax).  Both the HIP path and
 the CPU oracle consume the tensors it produces, bit for bit.
 
 The workloads are V4-shaped indexer inputs (StreamIndex: Memory-Bounded
@@ -196,3 +198,83 @@ def storage_numpy(t: torch.Tensor) -> np.ndarray:
     if t.dtype == torch.float8_e4m3fn:
         return t.view(torch.uint8).numpy()
     return t.numpy()
+
+
+# ------------------------------------------------------------ sparse attention
+
+@dataclass(frozen=True)
+class AttnWorkload:
+    """Sparse attention over n_sel selected compressed entries per row.
+
+    q [B,S,H,D], k and v [B,T,D] are bf16 with N(0, 1) entries.  Row t (at
+    absolute position row_offset + t) sees n = min(T, (pos + 1) // m)
+    compressed entries, the indexer's visibility rule; its index list holds
+    min(n_sel, n) distinct visible entries followed by -1 padding, the shape
+    of the indexer's output.  The pages give no attention dimensions; H = 64
+    heads of D = 128 mirror the indexer's.
+    """
+    name: str
+    B: int
+    S: int
+    T: int
+    H: int
+    D: int
+    n_sel: int
+    m: int = 4
+    row_offset: int = 0
+    scale: float = -1.0     # -1: 1 / sqrt(D)
+
+    @property
+    def softmax_scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.D)) if self.scale < 0 else self.scale
+
+    def with_(self, **kw) -> "AttnWorkload":
+        return replace(self, **kw)
+
+
+ATTN_WORKLOADS = {
+    # the indexer's S = 262,144 shape: the composite step at that length
+    "attn-s256k": AttnWorkload("attn-s256k", B=1, S=262144, T=65536, H=64, D=128, n_sel=2048),
+    "attn-s64k": AttnWorkload("attn-s64k", B=1, S=65536, T=16384, H=64, D=128, n_sel=2048),
+    "attn-small": AttnWorkload("attn-small", B=2, S=700, T=175, H=64, D=128, n_sel=100),
+}
+
+_AFFINE_P = 2_147_483_647  # prime: invertible modulo every visible count below it
+
+
+def make_attn_inputs(aw: AttnWorkload, seed: int = 0, device="cpu"):
+    """q [B,S,H,D], k, v [B,T,D] bf16 and idx [B,S,n_sel] int32 on ``device``.
+
+    Row t's list is (P * j + c_t) mod n for j < min(n_sel, n) with P prime
+    and c_t uniform in [0, n): distinct entries spread over the whole
+    visible range (the order is irrelevant to the attention), then -1.
+    """
+    B, S, T, H, D, L = aw.B, aw.S, aw.T, aw.H, aw.D, aw.n_sel
+    assert T < _AFFINE_P
+    q = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=device)
+    k = torch.empty((B, T, D), dtype=torch.bfloat16, device=device)
+    v = torch.empty((B, T, D), dtype=torch.bfloat16, device=device)
+    idx = torch.empty((B, S, L), dtype=torch.int32, device=device)
+    j = torch.arange(L, device=device, dtype=torch.int64)
+    for b in range(B):
+        gq = _generator(device, seed, 10 * b + 5)
+        gk = _generator(device, seed, 10 * b + 6)
+        gv = _generator(device, seed, 10 * b + 7)
+        gi = _generator(device, seed, 10 * b + 8)
+
+        def put_q(r0, r1, x, b=b):
+            q[b, r0:r1] = x.to(torch.bfloat16)
+
+        _rows(S, (H, D), "normal", gq, device, put_q)
+        k[b] = _draw((T, D), "normal", gk, device).to(torch.bfloat16)
+        v[b] = _draw((T, D), "normal", gv, device).to(torch.bfloat16)
+        for r0 in range(0, S, _ROW_CHUNK):
+            r1 = min(S, r0 + _ROW_CHUNK)
+            pos = torch.arange(r0, r1, device=device, dtype=torch.int64) + aw.row_offset
+            n = torch.clamp((pos + 1) // aw.m, max=T)
+            u = torch.rand((r1 - r0,), generator=gi, device=device, dtype=torch.float64)
+            c = torch.minimum((u * n).to(torch.int64), torch.clamp(n - 1, min=0))
+            sel = (_AFFINE_P * j[None, :] + c[:, None]) % torch.clamp(n, min=1)[:, None]
+            live = j[None, :] < torch.minimum(n, torch.tensor(L, device=device))[:, None]
+            idx[b, r0:r1] = torch.where(live, sel, torch.full_like(sel, -1)).to(torch.int32)
+    return {"q": q, "k": k, "v": v, "idx": idx}

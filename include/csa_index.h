@@ -1,5 +1,6 @@
 /*
- * csa_index.h -- C ABI of the MI355X (gfx950) CSA lightning-indexer top-k.
+ * csa_index.h -- C ABI of the MI355X (gfx950) CSA lightning-indexer top-k
+ * and of the sparse attention over the keys it selects.
  *
  * Operation (StreamIndex: Memory-Bounded Compressed Sparse Attention via
  * Streaming Top-k, Abstract): each query position rates every compressed key
@@ -166,6 +167,64 @@ int csa_plan_query(const csa_desc *desc, int32_t m, int32_t k,
 
 /* Static, human-readable text for a csa_status value. */
 const char *csa_status_string(int status);
+
+/* ------------------------------------------------------------------------
+ * Sparse attention over the selected keys.
+ *
+ * Operation (StreamIndex: Memory-Bounded Compressed Sparse Attention via
+ * Streaming Top-k, Abstract: once the indexer has chosen each query's keys,
+ * the attention kernel reads only those).  The page gives no formula; this
+ * entry point computes plain softmax attention restricted to the chosen
+ * compressed entries, with one key row and one value row per entry shared
+ * by all query heads:
+ *
+ *     E(b,t)  = entries e of idx[b,t,:] with 0 <= idx[b,t,e] < T
+ *     z_e     = scale * (q[b,t,h,:] . k[b, idx[b,t,e], :])
+ *     out[b,t,h,:] = sum_{e in E} softmax(z)_e * v[b, idx[b,t,e], :]
+ *     lse[b,t,h]   = log(sum_{e in E} exp(z_e))
+ *
+ * Entries outside [0, T) are padding (the indexer writes -1) and are never
+ * read.  Each valid entry counts once.  A row with no valid entry gets
+ * out = 0 and lse = -inf.  `idx` is typically csa_index's out_idx.
+ *
+ * Arithmetic: q.k products accumulate in fp32 on the matrix cores; the
+ * softmax runs in fp32 with a running maximum; the weights are rounded to
+ * bf16 for the weighted sum of v (fp32 accumulation); the normaliser is the
+ * fp32 sum of the unrounded weights; out is rounded to bf16 once.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Shapes of one sparse-attention call.
+ *   q    [B, S, H, D]   bf16   (device)
+ *   k    [B, T, D]      bf16   (device)
+ *   v    [B, T, D]      bf16   (device)
+ *   idx  [B, S, n_sel]  int32  (device)
+ *   out  [B, S, H, D]   bf16   (device)
+ *   lse  [B, S, H]      fp32   (device; may be NULL)
+ * Supported: H in {32, 64, 128}, D in {64, 128}; B >= 1, S >= 0, T >= 0,
+ * n_sel >= 0.  Other H or D return CSA_ERR_UNSUPPORTED.  q, k, v and out
+ * must be 16-byte aligned, idx and lse 4-byte aligned.
+ */
+typedef struct {
+    int64_t B;
+    int64_t S;
+    int64_t T;
+    int32_t H;
+    int32_t D;
+    int32_t n_sel;          /* index entries per query row (csa_index's k) */
+    int32_t reserved0;      /* must be 0 */
+} csa_attn_desc;
+
+/*
+ * csa_sparse_attention: softmax attention of every query row over the
+ * entries its index list selects (see above).  `scale` multiplies q.k (for
+ * example 1/sqrt(D)) and must be finite.  Writes only out and lse.  No
+ * device memory is allocated.  Deterministic: bitwise identical across runs.
+ * Returns CSA_OK or a negative csa_status; on error nothing is launched.
+ */
+int csa_sparse_attention(const void *q, const void *k, const void *v,
+                         const int32_t *idx, const csa_attn_desc *desc,
+                         float scale, void *out, float *lse, hipStream_t stream);
 
 #ifdef __cplusplus
 }

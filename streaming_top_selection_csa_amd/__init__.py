@@ -1,4 +1,5 @@
-"""MI355X-native CSA lightning-indexer top-k (streaming partition-merge).
+"""MI355X-native CSA lightning-indexer top-k (streaming partition-merge) and
+the sparse attention over the selected keys.
 
 The compute lives in libcsa_index.so (hand-written gfx950 HIP kernels behind
 the C ABI in include/csa_index.h); this package is its Python binding.
@@ -6,9 +7,9 @@ Importing it loads nothing; the library is loaded on first use and calls
 fail loudly if it is missing.
 """
 from .binding import (CSA_BF16, CSA_FP8_E4M3FN, CsaError, HipEvents, index, load_library,
-                      make_desc, make_options, plan_query, status_string, workspace_bytes,
-                      workspace_for)
+                      make_attn_desc, make_desc, make_options, plan_query, sparse_attention,
+                      status_string, workspace_bytes, workspace_for)
 
-__all__ = ["index", "plan_query", "workspace_bytes", "workspace_for", "load_library",
+__all__ = ["index", "sparse_attention", "make_attn_desc", "plan_query", "workspace_bytes", "workspace_for", "load_library",
            "status_string", "make_desc", "make_options", "CsaError", "HipEvents",
            "CSA_BF16", "CSA_FP8_E4M3FN"]

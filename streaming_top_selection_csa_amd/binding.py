@@ -9,6 +9,7 @@ built library or without a GPU tensor, calls fail.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from typing import Optional
 
@@ -27,7 +28,7 @@ CSA_BF16 = 0
 CSA_FP8_E4M3FN = 1
 
 EXPORTS = ("csa_index", "csa_index_ex", "csa_workspace_bytes", "csa_plan_query",
-           "csa_status_string")
+           "csa_status_string", "csa_sparse_attention")
 
 
 class CsaDesc(ctypes.Structure):
@@ -49,6 +50,12 @@ class CsaPlanInfo(ctypes.Structure):
                 ("chunk_keys", ctypes.c_int32), ("log_capacity", ctypes.c_int32),
                 ("grid", ctypes.c_int32), ("key_splits", ctypes.c_int32),
                 ("n_blocks", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class CsaAttnDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("S", ctypes.c_int64), ("T", ctypes.c_int64),
+                ("H", ctypes.c_int32), ("D", ctypes.c_int32), ("n_sel", ctypes.c_int32),
+                ("reserved0", ctypes.c_int32)]
 
 
 class CsaError(RuntimeError):
@@ -81,6 +88,9 @@ def load_library():
     lib.csa_plan_query.argtypes = [ctypes.POINTER(CsaDesc), i32, i32, ctypes.POINTER(CsaOptions),
                                    ctypes.POINTER(CsaPlanInfo)]
     lib.csa_plan_query.restype = ctypes.c_int
+    lib.csa_sparse_attention.argtypes = [vp, vp, vp, vp, ctypes.POINTER(CsaAttnDesc),
+                                         ctypes.c_float, vp, vp, vp]
+    lib.csa_sparse_attention.restype = ctypes.c_int
     lib.csa_status_string.argtypes = [ctypes.c_int]
     lib.csa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -203,6 +213,57 @@ def index(q: torch.Tensor, w: torch.Tensor, k_cmp: torch.Tensor, m: int, k: int,
     return out_idx, out_score
 
 
+def make_attn_desc(B, S, T, H, D, n_sel) -> CsaAttnDesc:
+    return CsaAttnDesc(int(B), int(S), int(T), int(H), int(D), int(n_sel), 0)
+
+
+def sparse_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
+                     scale: Optional[float] = None, *, out: Optional[torch.Tensor] = None,
+                     lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+                     stream: Optional[torch.cuda.Stream] = None):
+    """Softmax attention of every query row over its selected compressed
+    entries (csa_sparse_attention).
+
+    q [B,S,H,D] bf16, k and v [B,T,D] bf16, idx [B,S,n_sel] int32 (entries
+    outside [0, T) are padding; csa_index's out_idx fits).  `scale`
+    multiplies q.k (default 1/sqrt(D)).  Returns (out bf16 [B,S,H,D],
+    lse fp32 [B,S,H] or None).  Asynchronous on `stream`.
+    """
+    lib = load_library()
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, name, torch.bfloat16)
+    _check(idx, "idx", torch.int32)
+    if q.dim() != 4 or k.dim() != 3 or v.dim() != 3 or idx.dim() != 3:
+        raise ValueError("expected q [B,S,H,D], k and v [B,T,D], idx [B,S,n_sel]")
+    B, S, H, D = q.shape
+    T = k.shape[1]
+    if tuple(k.shape) != (B, T, D) or tuple(v.shape) != (B, T, D) or tuple(idx.shape[:2]) != (B, S):
+        raise ValueError("inconsistent shapes of q, k, v, idx")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=q.device)
+    _check(out, "out", torch.bfloat16)
+    if tuple(out.shape) != (B, S, H, D):
+        raise ValueError("out must be [B,S,H,D]")
+    if lse is None and want_lse:
+        lse = torch.empty((B, S, H), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check(lse, "lse", torch.float32)
+        if tuple(lse.shape) != (B, S, H):
+            raise ValueError("lse must be [B,S,H]")
+    desc = make_attn_desc(B, S, T, H, D, idx.shape[2])
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    rc = lib.csa_sparse_attention(q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(),
+                                  ctypes.byref(desc), float(scale), out.data_ptr(),
+                                  lse.data_ptr() if lse is not None else None,
+                                  ctypes.c_void_p(stream.cuda_stream))
+    if rc != CSA_OK:
+        raise CsaError(rc, "csa_sparse_attention")
+    return out, lse
+
+
 def workspace_for(q: torch.Tensor, k_cmp: torch.Tensor, m: int, k: int, chunk_keys: int = 0,
                   row_offset: int = 0, key_splits: int = 0) -> torch.Tensor:
     """A torch-allocated workspace big enough for `index` on these inputs."""
@@ -218,7 +279,7 @@ def workspace_for(q: torch.Tensor, k_cmp: torch.Tensor, m: int, k: int, chunk_ke
 
 class HipEvents:
     """Raw hipEvent_t pairs from the HIP runtime torch already loaded, for
-    timing the scoring kernel on the stream it runs on."""
+    timing a kernel on the stream it runs on."""
 
     def __init__(self, n: int):
         self._hip = ctypes.CDLL("libamdhip64.so")
@@ -226,12 +287,18 @@ class HipEvents:
         self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
                                                   ctypes.c_void_p, ctypes.c_void_p]
         self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self._hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.pairs = []
         for _ in range(n):
             a, b = ctypes.c_void_p(), ctypes.c_void_p()
             if self._hip.hipEventCreate(ctypes.byref(a)) or self._hip.hipEventCreate(ctypes.byref(b)):
                 raise RuntimeError("hipEventCreate failed")
             self.pairs.append((a.value, b.value))
+
+    def record(self, event, stream: torch.cuda.Stream):
+        """Record raw event `event` on `stream` (hipEventRecord)."""
+        if self._hip.hipEventRecord(ctypes.c_void_p(event), ctypes.c_void_p(stream.cuda_stream)):
+            raise RuntimeError("hipEventRecord failed")
 
     def elapsed_ms(self, i: int) -> float:
         ms = ctypes.c_float()

@@ -163,3 +163,43 @@ extern "C" int csa_index(const void *q, const float *w, const void *k_cmp,
 {
     return csa_index_ex(q, w, k_cmp, desc, m, k, out_idx, out_score, nullptr, stream);
 }
+
+extern "C" int csa_sparse_attention(const void *q, const void *k, const void *v,
+                                    const int32_t *idx, const csa_attn_desc *desc, float scale,
+                                    void *out, float *lse, hipStream_t stream)
+{
+    if (!desc) return CSA_ERR_INVALID_ARG;
+    const csa_attn_desc &d = *desc;
+    if (d.B < 1 || d.S < 0 || d.T < 0 || d.n_sel < 0 || d.reserved0 != 0)
+        return CSA_ERR_INVALID_ARG;
+    if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return CSA_ERR_INVALID_ARG;
+    if (!((d.H == 32 || d.H == 64 || d.H == 128) && (d.D == 64 || d.D == 128)))
+        return CSA_ERR_UNSUPPORTED;
+    // element counts must stay addressable with 64-bit byte offsets
+    constexpr int64_t kMaxElems = int64_t(1) << 56;
+    if (d.S > kMaxElems / d.B || d.T > kMaxElems / d.B) return CSA_ERR_INVALID_ARG;
+    const int64_t rows = d.B * d.S;
+    if (rows > kMaxElems / (int64_t(d.H) * d.D) || (d.n_sel > 0 && rows > kMaxElems / d.n_sel) ||
+        d.B * d.T > kMaxElems / d.D)
+        return CSA_ERR_INVALID_ARG;
+    if (rows == 0) return CSA_OK;
+    if (!q || !out || (d.n_sel > 0 && !idx) || (d.T > 0 && (!k || !v)))
+        return CSA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+        !aligned(idx, 4) || !aligned(lse, 4))
+        return CSA_ERR_INVALID_ARG;
+
+    csa::AttnArgs a;
+    a.q = static_cast<const unsigned char *>(q);
+    a.k = static_cast<const unsigned char *>(k);
+    a.v = static_cast<const unsigned char *>(v);
+    a.idx = idx;
+    a.out = static_cast<unsigned char *>(out);
+    a.lse = lse;
+    a.B = d.B;
+    a.S = d.S;
+    a.T = d.T;
+    a.n_sel = d.n_sel;
+    a.scale = scale;
+    return csa::launch_sparse_attention(a, d.H, d.D, stream) == hipSuccess ? CSA_OK : CSA_ERR_HIP;
+}

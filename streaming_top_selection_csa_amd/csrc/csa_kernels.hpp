@@ -40,4 +40,20 @@ hipError_t launch_merge_splits(const Plan &p, const int32_t *part_idx, const flo
 hipError_t launch_sort_rows(const Plan &p, int32_t *out_idx, float *out_score, int num_cus,
                             hipStream_t s);
 
+// Arguments of the sparse-attention kernel (device pointers, row-major).
+struct AttnArgs {
+    const unsigned char *q;     // [B, S, H, D] bf16
+    const unsigned char *k;     // [B, T, D] bf16
+    const unsigned char *v;     // [B, T, D] bf16
+    const int32_t *idx;         // [B, S, n_sel]; entries outside [0, T) are padding
+    unsigned char *out;         // [B, S, H, D] bf16
+    float *lse;                 // [B, S, H] or null
+    int64_t B, S, T;
+    int n_sel;
+    float scale;                // multiplies q . k
+};
+
+// H in {32, 64, 128}, D in {64, 128}; anything else is hipErrorInvalidValue.
+hipError_t launch_sparse_attention(const AttnArgs &a, int H, int D, hipStream_t s);
+
 }  // namespace csa

@@ -132,3 +132,63 @@ def compare_tolerant(g_idx, g_score, o_idx, o_score, score_fn, t_rows, T, m, rto
         off += kept
     return {"max_rel_err": max_rel, "swaps": swaps,
             "recall": hits / total if total else 1.0, "recall_min": recall_min}
+
+
+# ------------------------------------------------------------ sparse attention
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def attention_reference(inp, b, rows, scale):
+    """Oracle outputs for rows `rows` of batch entry b of an attention input
+    dict (q, k, v, idx on any device), plus the bound on the score error.
+
+    Score error: each q.k is an fp32 sum of D exact bf16 products, whatever
+    the summation order within D*2^-24 * sum_x |q_x k_x|, which is at most
+    D*2^-24 * |q| |k| (Cauchy-Schwarz); dz is that times |scale|, maximised
+    over the row's valid entries.
+    """
+    q = storage_numpy(inp["q"][b, torch.as_tensor(rows, device=inp["q"].device)])
+    k = storage_numpy(inp["k"][b])
+    v = storage_numpy(inp["v"][b])
+    idx = inp["idx"][b, torch.as_tensor(rows, device=inp["idx"].device)].cpu().numpy()
+    o, lse, a = oracle.sparse_attention(q, k, v, idx, scale)
+    T, D = k.shape
+    qn = np.linalg.norm(bf16_to_f64(q), axis=-1)                       # [n, H]
+    kn = np.linalg.norm(bf16_to_f64(k), axis=-1) if T > 0 else np.zeros(0)
+    valid = (idx >= 0) & (idx < T)
+    kmax = np.array([kn[r[v_]].max() if v_.any() else 0.0 for r, v_ in zip(idx, valid)])
+    dz = abs(scale) * D * 2.0 ** -24 * qn * kmax[:, None]              # [n, H]
+    return o, lse, a, dz
+
+
+def compare_attention(g_out, g_lse, o, lse, a, dz):
+    """GPU rows (bf16 out [n,H,D] as uint16 bits, fp32 lse [n,H]) against
+    the oracle.  Bound per element, from the kernel's arithmetic:
+      * weights rounded to bf16 for the value sum: <= 2^-9 * a, with
+        a = sum_e p_e |v_e| (the normaliser uses unrounded weights);
+      * score error dz moves o by at most 2 * dz * a (d o / d z_e =
+        p_e (v_e - o));
+      * fp32 accumulation and the final bf16 rounding: <= 2^-9 * |o| plus
+        terms far below the first;
+    so |out - o| <= 2^-8 * (a + |o|) + 2 * dz * a (a factor 2 of margin on
+    the rounding terms).  lse: |lse' - lse| <= dz + 2^-20 * (1 + |lse|).
+    Rows without valid entries must be exactly 0 with lse = -inf.
+    """
+    out = bf16_to_f64(g_out)
+    empty = np.isneginf(lse)
+    assert np.array_equal(np.isneginf(g_lse), empty), "empty rows differ"
+    assert np.all(out[empty] == 0), "empty rows must be zero"
+    tol = 2.0 ** -8 * (a + np.abs(o)) + 2 * dz[..., None] * a
+    err = np.abs(out - o)
+    bad = err > tol
+    assert not bad.any(), (f"{bad.sum()} elements out of bound; worst excess "
+                           f"{(err - tol).max():.3e} at {np.unravel_index((err - tol).argmax(), err.shape)}")
+    fin = ~empty
+    ltol = dz[fin] + 2.0 ** -20 * (1 + np.abs(lse[fin]))
+    lerr = np.abs(g_lse[fin].astype(np.float64) - lse[fin])
+    assert np.all(lerr <= ltol), f"lse off by {lerr.max():.3e}"
+    rel = err[fin] / np.maximum(a[fin], 1e-30)
+    return {"max_err_over_a": float(rel.max()) if rel.size else 0.0,
+            "max_lse_err": float(lerr.max()) if lerr.size else 0.0}

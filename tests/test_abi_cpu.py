@@ -196,3 +196,44 @@ def test_bench_visible_pairs_closed_form():
         assert bench.visible_pairs(S, T, m, 1, off) == direct, (S, T, m, off)
     # the headline shape: m*T*(T-1)/2 + T with S = m*T
     assert bench.visible_pairs(262144, 65536, 4) == 4 * 65536 * 65535 // 2 + 65536
+
+
+def attn_call(lib, desc, scale=0.125, q=16, k=16, v=16, idx=16, out=16, lse=None):
+    """csa_sparse_attention with fake (never dereferenced) pointers: every
+    case below must be rejected before anything touches the device."""
+    vp = ctypes.c_void_p
+    return lib.csa_sparse_attention(vp(q) if q else None, vp(k) if k else None,
+                                    vp(v) if v else None, vp(idx) if idx else None,
+                                    ctypes.byref(desc) if desc is not None else None,
+                                    ctypes.c_float(scale), vp(out) if out else None,
+                                    vp(lse) if lse else None, None)
+
+
+def test_sparse_attention_validation(lib):
+    E = B.CSA_ERR_INVALID_ARG
+    U = B.CSA_ERR_UNSUPPORTED
+    ok = csa.make_attn_desc(1, 4, 10, 64, 128, 8)
+    assert attn_call(lib, None) == E
+    for H, D in [(16, 128), (64, 32), (96, 128), (64, 256), (1, 64)]:
+        assert attn_call(lib, csa.make_attn_desc(1, 4, 10, H, D, 8)) == U, (H, D)
+    for args in [(0, 4, 10, 64, 128, 8), (1, -1, 10, 64, 128, 8), (1, 4, -1, 64, 128, 8),
+                 (1, 4, 10, 64, 128, -1)]:
+        assert attn_call(lib, csa.make_attn_desc(*args)) == E, args
+    r = csa.make_attn_desc(1, 4, 10, 64, 128, 8)
+    r.reserved0 = 1
+    assert attn_call(lib, r) == E
+    assert attn_call(lib, ok, scale=float("nan")) == E
+    assert attn_call(lib, ok, scale=float("inf")) == E
+    assert attn_call(lib, ok, q=0) == E
+    assert attn_call(lib, ok, out=0) == E
+    assert attn_call(lib, ok, idx=0) == E
+    assert attn_call(lib, ok, k=0) == E and attn_call(lib, ok, v=0) == E
+    assert attn_call(lib, ok, q=24) == E      # not 16-byte aligned
+    assert attn_call(lib, ok, out=8) == E
+    assert attn_call(lib, ok, idx=18) == E    # not 4-byte aligned
+    assert attn_call(lib, ok, lse=2) == E
+    # sizes whose byte offsets would overflow
+    assert attn_call(lib, csa.make_attn_desc(1 << 20, 1 << 40, 10, 64, 128, 8)) == E
+    # nothing to do: no rows (no pointer is needed)
+    assert attn_call(lib, csa.make_attn_desc(1, 0, 10, 64, 128, 8), q=0, k=0, v=0, idx=0,
+                     out=0) == B.CSA_OK
