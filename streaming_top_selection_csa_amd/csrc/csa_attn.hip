@@ -8,25 +8,29 @@
 // scale * q[r,h,:] . k[idx[e],:], applied to v[idx[e],:]; every head shares
 // the compressed key and value rows.
 //
-// One workgroup per query row, one wave per 32 heads.  The row's selected
-// entries are taken 32 at a time: the workgroup gathers the 32 key rows and
-// 32 value rows (each a contiguous D*2-byte row; 16 lanes per row, so every
-// load is a full row segment) into LDS, then every wave
+// One workgroup per query row, one wave per 32 heads.  The row's index list
+// is staged in LDS (1,024 entries at a time); its entries are taken 32 at a
+// time (a tile).  Every tile's 32 key rows and 32 value rows stream from
+// global memory straight into LDS (global_load_lds, 16 bytes per lane) into a
+// ring of three buffers, two tiles ahead, so 32 KB of gathers per workgroup
+// stay in flight without passing through registers.  Each row's 16-byte
+// chunks are XOR-swizzled by row, so the MFMA operand reads below (32 rows,
+// one chunk each) hit distinct LDS banks.  For every tile each wave
 //   * computes the 32x32 block S^T = K_tile . Q^T of (key, head) scores with
-//     v_mfma_f32_32x32x16_bf16: A = the key rows from LDS, B = the wave's 32
+//     v_mfma_f32_32x32x16_bf16: A = key rows from LDS, B = the wave's 32
 //     query heads, held in registers for the whole row;
 //   * runs the online softmax: in the MFMA output layout each lane holds one
 //     head (lane % 32) and 16 of the tile's keys, so the running maximum and
 //     the sum stay in the lane, and the two lanes of a head agree through one
 //     v_permlane32_swap;
-//   * accumulates O^T += V_tile^T . P^T: B = the bf16 weights straight from
-//     the lane's score registers, A = the value tile, stored transposed in
-//     LDS with the tile's keys permuted so that each lane's eight keys of a
-//     K step are the eight keys its weights belong to.
-// The gather of the next tile is issued before the current tile's MFMA work
-// and lands in registers, so the (mostly L2 / MALL) gather latency overlaps
-// compute.  Rows are mapped to workgroups so that consecutive rows share an
-// XCD (and its L2): queries close in position tend to pick the same keys.
+//   * turns the row-major value rows into the key-contiguous operand layout
+//     the weighted sum needs with an MFMA against a bf16 identity (exact):
+//     V_tile . I lands with each lane holding one value column and the same
+//     16 keys its weights belong to;
+//   * accumulates O^T += V_tile^T . P^T with B = the bf16 weights straight
+//     from the lane's score registers.
+// Rows are mapped to workgroups so that consecutive rows share an XCD (and
+// its L2): queries close in position tend to pick the same keys.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -71,15 +75,13 @@ __device__ __forceinline__ float pair_sum(float x)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Position of tile key `key` in a transposed value row.  The PV product's K
-// step j pairs lane half hh, element e with key 16j + 8(e/4) + 4hh + e%4 (the
-// keys that score-output element 8j + e of that lane half holds); swapping
-// bits 2 and 3 of the key puts those eight keys at 16j + 8hh + e, one 16-byte
-// read.
-__device__ __forceinline__ int vt_pos(int key)
-{
-    return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
-}
+// s_waitcnt immediate: at most n vector-memory loads of this wave in flight,
+// no LDS / scalar access outstanding (lgkmcnt 0), export count untouched.
+constexpr int vm_wait_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4); }
+
+constexpr int kSeg = 1024;  // index-list entries staged in LDS at a time
+constexpr int kBuf = 3;     // LDS ring of key/value tiles
+constexpr int kAhead = 2;   // tiles in flight ahead of the one being computed
 
 template <int H, int D>
 __global__ void __launch_bounds__(64 * (H / 32))
@@ -87,19 +89,18 @@ sparse_attn_kernel(AttnArgs a, int64_t row0, int64_t nrows)
 {
     constexpr int W = H / 32;              // waves; wave w owns heads 32w .. 32w+31
     constexpr int NT = 64 * W;
-    constexpr int CH = D / 8;              // 16-byte chunks per key or value row
-    constexpr int PER_KEY = 2 * CH;        // chunks of one entry (key row + value row)
-    constexpr int KPP = NT / PER_KEY;      // entries gathered per pass of the workgroup
-    constexpr int NLD = KT / KPP;          // gather passes per tile
+    constexpr int ROWB = 2 * D;            // bytes of one key or value row
+    constexpr int NC = ROWB / 16;          // 16-byte chunks per row
+    constexpr int HALF = KT * ROWB;        // bytes of the tile's key (or value) rows
+    constexpr int NBLK = 2 * HALF / 1024;  // 1 KB DMA blocks per tile
+    constexpr int BPW = NBLK / W;          // DMA blocks (loads) per wave per tile
     constexpr int KS = D / 16;             // K steps of the score product
     constexpr int MB = D / 32;             // 32-row blocks of the output
-    constexpr int KROW = 2 * D + 16;       // LDS bytes per key row (16-byte pad)
-    constexpr int VROW = 2 * KT + 16;      // LDS bytes per transposed value row
-    static_assert(NT % PER_KEY == 0 && KT % KPP == 0, "gather layout");
+    static_assert(NBLK % W == 0 && BPW <= 32, "DMA layout");
+    static_assert(kBuf == kAhead + 1, "ring");
 
-    __shared__ __attribute__((aligned(16))) unsigned char s_k[KT * KROW];
-    __shared__ __attribute__((aligned(16))) unsigned char s_v[D * VROW];
-    __shared__ int s_valid[KT];
+    __shared__ __attribute__((aligned(1024))) unsigned char s_ring[kBuf][2 * HALF];
+    __shared__ int s_idx[kSeg];
 
     // consecutive rows on one XCD: workgroup i runs on XCD i % 8
     const int64_t per_xcd = (nrows + kXcds - 1) / kXcds;
@@ -110,65 +111,30 @@ sparse_attn_kernel(AttnArgs a, int64_t row0, int64_t nrows)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hh = lane >> 5;              // lane half: K slice of MFMA operands
     const int col = lane & 31;
-    const int head = 32 * (tid >> 6) + col;
+    const int head = 32 * wave + col;
 
     // B operand of the score product: q[row, head, 16s + 8hh .. +8]
     bf16x8_t qop[KS];
     {
-        const unsigned char *qr = a.q + (row * H + head) * int64_t(2 * D) + 16 * hh;
+        const unsigned char *qr = a.q + (row * H + head) * int64_t(ROWB) + 16 * hh;
 #pragma unroll
         for (int s = 0; s < KS; ++s) qop[s] = as_op(*reinterpret_cast<const u32x4_t *>(qr + 32 * s));
     }
+    // B operand of the transposition: identity over one 32-column block;
+    // lane (hh, col) holds rows 16s + 8hh + e of column col
+    bf16x8_t ident[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ident[s][e] = __bf16(16 * s + 8 * hh + e == col ? 1.f : 0.f);
 
-    // gather role: this thread moves 16-byte chunk `ch` of the key row (or of
-    // the value row) of entries i*KPP + ent, i < NLD, of every tile
-    const int part = tid % PER_KEY;
-    const int ent = tid / PER_KEY;
-    const bool is_v = part >= CH;
-    const int ch = is_v ? part - CH : part;
-    const unsigned char *src = (is_v ? a.v : a.k) + b * a.T * int64_t(2 * D) + 16 * ch;
+    const unsigned char *kbase = a.k + b * a.T * int64_t(ROWB);
+    const unsigned char *vbase = a.v + b * a.T * int64_t(ROWB);
     const int32_t *list = a.idx + row * int64_t(a.n_sel);
-    const int n_sel = a.n_sel;
     const int64_t T = a.T;
-    const int ntiles = (n_sel + KT - 1) / KT;
-
-    int cur[NLD], nxt[NLD];
-    u32x4_t stage[NLD];
-
-    auto load_ids = [&](int tile, int *ids) {
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            const int pos = tile * KT + i * KPP + ent;
-            int s = pos < n_sel ? list[pos] : -1;
-            ids[i] = (s >= 0 && s < T) ? s : -1;
-        }
-    };
-    auto gather = [&](const int *ids) {
-#pragma unroll
-        for (int i = 0; i < NLD; ++i)
-            stage[i] = ids[i] >= 0 ? *reinterpret_cast<const u32x4_t *>(src + int64_t(ids[i]) * (2 * D))
-                                   : u32x4_t{0, 0, 0, 0};
-    };
-    auto to_lds = [&](const int *ids) {
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            const int key = i * KPP + ent;
-            if (!is_v) {
-                *reinterpret_cast<u32x4_t *>(s_k + key * KROW + 16 * ch) = stage[i];
-                if (ch == 0) s_valid[key] = ids[i] >= 0;
-            } else {
-                unsigned char *dst = s_v + (8 * ch) * VROW + 2 * vt_pos(key);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const unsigned x = stage[i][e];
-                    *reinterpret_cast<uint16_t *>(dst + (2 * e) * VROW) = uint16_t(x);
-                    *reinterpret_cast<uint16_t *>(dst + (2 * e + 1) * VROW) = uint16_t(x >> 16);
-                }
-            }
-        }
-    };
 
     f32x16_t acc[MB];
 #pragma unroll
@@ -179,36 +145,76 @@ sparse_attn_kernel(AttnArgs a, int64_t row0, int64_t nrows)
     float l_run = 0.f;        // this lane's part of the running sum of weights
     const float c = a.scale * kLog2e;
 
-    load_ids(0, cur);
-    gather(cur);
-    load_ids(1, nxt);
-    to_lds(cur);
-    __syncthreads();
+    // tile `t` of the staged segment into ring buffer `buf`: this wave's
+    // blocks j = wave + v*W; block j < NBLK/2 holds key rows, the rest value
+    // rows; the lane's 16 bytes land at chunk p of row r and carry the row's
+    // logical chunk p ^ (r % NC).  Padding entries load row 0 (never used).
+    auto dma_tile = [&](int t, int buf) {
+#pragma unroll
+        for (int v = 0; v < BPW; ++v) {
+            const int j = wave + v * W;
+            const bool is_v = j >= NBLK / 2;
+            const int off = (is_v ? j - NBLK / 2 : j) * 1024 + lane * 16;
+            const int r = off / ROWB;
+            const int p = (off % ROWB) / 16;
+            const int s = s_idx[t * KT + r];
+            const unsigned char *src = (is_v ? vbase : kbase) +
+                                       int64_t(s >= 0 ? s : 0) * ROWB + 16 * (p ^ (r % NC));
+            __builtin_amdgcn_global_load_lds(
+                src, (__attribute__((address_space(3))) void *)&s_ring[buf][j * 1024], 16, 0, 0);
+        }
+    };
 
-    for (int it = 0; it < ntiles; ++it) {
-        const bool more = it + 1 < ntiles;
-        if (more) gather(nxt);  // in flight during this tile's work
-        int later[NLD];
-        load_ids(it + 2, later);
+    for (int seg0 = 0; seg0 < a.n_sel && T > 0; seg0 += kSeg) {
+        const int nseg = a.n_sel - seg0 < kSeg ? a.n_sel - seg0 : kSeg;
+        const int ntiles = (nseg + KT - 1) / KT;
+        __syncthreads();  // the previous segment is done with s_idx and the ring
+        for (int i = tid; i < ntiles * KT; i += NT) {
+            const int s = i < nseg ? list[seg0 + i] : -1;
+            s_idx[i] = (s >= 0 && s < T) ? s : -1;
+        }
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));  // nothing but tile loads in flight below
+        __syncthreads();
 
-        const uint32_t vmask =
-            uint32_t(__builtin_amdgcn_ballot_w64(s_valid[col] != 0));  // bit = tile key
-        if (vmask != 0) {
+        for (int t = 0; t < kAhead && t < ntiles; ++t) dma_tile(t, t);
+        for (int t = 0; t < ntiles; ++t) {
+            const int buf = t % kBuf;
+            // this wave's loads of tile t done (those of tile t+1 may fly),
+            // then every wave's
+            if (t + 1 < ntiles)
+                __builtin_amdgcn_s_waitcnt(vm_wait_imm(BPW));
+            else
+                __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+            __builtin_amdgcn_s_barrier();
+            __asm__ volatile("" ::: "memory");
+            // every wave is past tile t-1: its buffer takes tile t+2
+            if (t + kAhead < ntiles) dma_tile(t + kAhead, (t + kAhead) % kBuf);
+
+            const uint32_t vmask =
+                uint32_t(__builtin_amdgcn_ballot_w64(s_idx[t * KT + col] >= 0));  // bit = tile key
+            if (vmask == 0) continue;
+            const unsigned char *kt = &s_ring[buf][0];
+            const unsigned char *vt = &s_ring[buf][HALF];
+            const int swz = col % NC;
             // S^T[key][head] for the tile's 32 keys and the wave's 32 heads
-            f32x16_t sc;
+            f32x16_t s0, s1;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sc[i] = 0.f;
-            const unsigned char *krow = s_k + col * KROW + 16 * hh;
+            for (int i = 0; i < 16; ++i) s0[i] = s1[i] = 0.f;
 #pragma unroll
-            for (int s = 0; s < KS; ++s)
-                sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_op(krow + 32 * s), qop[s], sc, 0,
-                                                             0, 0);
+            for (int s = 0; s < KS; s += 2) {
+                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    lds_op(kt + col * ROWB + 16 * ((2 * s + hh) ^ swz)), qop[s], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    lds_op(kt + col * ROWB + 16 * ((2 * s + 2 + hh) ^ swz)), qop[s + 1], s1, 0, 0,
+                    0);
+            }
             // lane holds head `col`, keys 8(i/4) + 4hh + i%4
+            float sc[16];
             float tmax = -INFINITY;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int key = 8 * (i >> 2) + 4 * hh + (i & 3);
-                sc[i] = ((vmask >> key) & 1u) ? sc[i] * c : -INFINITY;
+                sc[i] = ((vmask >> key) & 1u) ? (s0[i] + s1[i]) * c : -INFINITY;
                 tmax = fmaxf(tmax, sc[i]);
             }
             tmax = pair_max(tmax);
@@ -230,26 +236,32 @@ sparse_attn_kernel(AttnArgs a, int64_t row0, int64_t nrows)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) acc[mb][i] *= alpha;
             }
-            // O^T[dv][head] += V^T[dv][keys] . P^T[keys][head]
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int mb = 0; mb < MB; ++mb) {
+                // V_tile[keys][32mb ..] . I: lane gets column 32mb + col at
+                // the keys of its score registers, exactly
+                f32x16_t tv;
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-                    acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        lds_op(s_v + (32 * mb + col) * VROW + 32 * j + 16 * hh), pb[j], acc[mb],
+                for (int i = 0; i < 16; ++i) tv[i] = 0.f;
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    tv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        lds_op(vt + col * ROWB + 16 * ((4 * mb + 2 * s + hh) ^ swz)), ident[s], tv,
                         0, 0, 0);
-        }
-        __syncthreads();  // every wave is done with the tile
-        if (more) to_lds(nxt);
+                bf16x8_t va[2];
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) nxt[i] = later[i];
-        __syncthreads();
+                for (int i = 0; i < 16; ++i) va[i >> 3][i & 7] = __bf16(tv[i]);
+                // O^T[dv][head] += V^T[dv][keys] . P^T[keys][head]
+                acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[0], pb[0], acc[mb], 0, 0, 0);
+                acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[1], pb[1], acc[mb], 0, 0, 0);
+            }
+        }
     }
 
     // epilogue: lane holds head `col`, rows dv = 32mb + 8(i/4) + 4hh + i%4
     const float l_tot = pair_sum(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    unsigned char *orow = a.out + (row * H + head) * int64_t(2 * D);
+    unsigned char *orow = a.out + (row * H + head) * int64_t(ROWB);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
