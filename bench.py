@@ -41,6 +41,8 @@ METRIC = "indexer queries/sec + MFMA TFLOP/s (% peak) + peak HBM GB at S=262K, 1
 PEAK_TFLOPS = {"bf16": 2500.0, "e4m3fn": 5000.0}   # MI355X dense MFMA
 KERNEL_SRC = os.path.join(ROOT, "streaming_top_selection_csa_amd", "csrc", "csa_stream.hpp")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "stream_topk_s256k_pmc.md")
+ATTN_SRC = os.path.join(ROOT, "streaming_top_selection_csa_amd", "csrc", "csa_attn.hip")
+ATTN_PMC_SUMMARY = os.path.join(ROOT, "profiles", "sparse_attn_s256k_pmc.md")
 
 
 def visible_pairs(S, T, m, B=1, row_offset=0):
@@ -61,21 +63,22 @@ def visible_pairs(S, T, m, B=1, row_offset=0):
     return B * (G(row_offset + S) - G(row_offset))
 
 
-def kernel_sha():
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_sha(src=KERNEL_SRC):
+    with open(src, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def traffic_from_profile(workload):
-    """HBM bytes per scoring launch from the committed counter summary, if it
-    was taken on this kernel source and workload."""
-    if not os.path.exists(PMC_SUMMARY):
+def traffic_from_profile(workload, summary=PMC_SUMMARY, src=KERNEL_SRC):
+    """Bytes per launch beyond L2 (HBM and memory-side cache) from a
+    committed counter summary, if it was taken on this kernel source and
+    workload."""
+    if not os.path.exists(summary):
         return None
-    text = open(PMC_SUMMARY).read()
+    text = open(summary).read()
     sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
     wl = re.search(r"workload:\s*(\S+)", text)
     tb = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not (sha and wl and tb) or sha.group(1) != kernel_sha() or wl.group(1) != workload:
+    if not (sha and wl and tb) or sha.group(1) != kernel_sha(src) or wl.group(1) != workload:
         return None
     return float(tb.group(1))
 
@@ -217,7 +220,8 @@ def attention(csa, args):
         "peak_hbm_gb": peak_hbm / 1e9,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS["bf16"],
                      "unit": "TFLOP/s", "frac": achieved / PEAK_TFLOPS["bf16"],
-                     "traffic": None, "algorithmic_io_gb": io / 1e9,
+                     "traffic": traffic_from_profile(aw.name, ATTN_PMC_SUMMARY, ATTN_SRC),
+                     "algorithmic_io_gb": io / 1e9,
                      "gathered_gb": gathered / 1e9},
         "cpu_baseline": cpu,
     }

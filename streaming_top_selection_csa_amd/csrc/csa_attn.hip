@@ -12,10 +12,10 @@
 // is staged in LDS (1,024 entries at a time); its entries are taken 32 at a
 // time (a tile).  Every tile's 32 key rows and 32 value rows stream from
 // global memory straight into LDS (global_load_lds, 16 bytes per lane) into a
-// ring of three buffers, two tiles ahead, so 32 KB of gathers per workgroup
-// stay in flight without passing through registers.  Each row's 16-byte
-// chunks are XOR-swizzled by row, so the MFMA operand reads below (32 rows,
-// one chunk each) hit distinct LDS banks.  For every tile each wave
+// ring of two buffers, one tile ahead; at 36 KB of LDS four workgroups share
+// a CU (more resident waves beat deeper rings here).  Each row's 16-byte
+// chunks are XOR-swizzled by row, so the operand reads below hit distinct
+// LDS banks.  For every tile each wave
 //   * computes the 32x32 block S^T = K_tile . Q^T of (key, head) scores with
 //     v_mfma_f32_32x32x16_bf16: A = key rows from LDS, B = the wave's 32
 //     query heads, held in registers for the whole row;
@@ -23,12 +23,10 @@
 //     head (lane % 32) and 16 of the tile's keys, so the running maximum and
 //     the sum stay in the lane, and the two lanes of a head agree through one
 //     v_permlane32_swap;
-//   * turns the row-major value rows into the key-contiguous operand layout
-//     the weighted sum needs with an MFMA against a bf16 identity (exact):
-//     V_tile . I lands with each lane holding one value column and the same
-//     16 keys its weights belong to;
 //   * accumulates O^T += V_tile^T . P^T with B = the bf16 weights straight
-//     from the lane's score registers.
+//     from the lane's score registers and A read from the row-major value
+//     rows with gfx950's LDS transpose load (ds_read_b64_tr_b16), which
+//     hands each lane one value column at the keys its weights belong to.
 // Rows are mapped to workgroups so that consecutive rows share an XCD (and
 // its L2): queries close in position tend to pick the same keys.
 #include <hip/hip_runtime.h>
@@ -45,6 +43,8 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef short s4_t __attribute__((ext_vector_type(4)));
+typedef short s8_t __attribute__((ext_vector_type(8)));
 
 constexpr int KT = 32;                 // selected entries per tile
 constexpr int kXcds = 8;               // XCDs of an MI355X; workgroups go round-robin
@@ -80,8 +80,20 @@ __device__ __forceinline__ float pair_sum(float x)
 constexpr int vm_wait_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4); }
 
 constexpr int kSeg = 1024;  // index-list entries staged in LDS at a time
-constexpr int kBuf = 3;     // LDS ring of key/value tiles
-constexpr int kAhead = 2;   // tiles in flight ahead of the one being computed
+constexpr int kBuf = 2;     // LDS ring of key/value tiles (36 KB: four workgroups per CU)
+constexpr int kAhead = 1;   // tiles in flight ahead of the one being computed
+
+// Waits until this wave has at most `later` tiles of BPW loads in flight.
+template <int BPW>
+__device__ __forceinline__ void wait_tiles(int later)
+{
+    if (later >= 2)
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * BPW));
+    else if (later == 1)
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(BPW));
+    else
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+}
 
 template <int H, int D>
 __global__ void __launch_bounds__(64 * (H / 32))
@@ -97,7 +109,7 @@ sparse_attn_kernel(AttnArgs a, int64_t row0, int64_t nrows)
     constexpr int KS = D / 16;             // K steps of the score product
     constexpr int MB = D / 32;             // 32-row blocks of the output
     static_assert(NBLK % W == 0 && BPW <= 32, "DMA layout");
-    static_assert(kBuf == kAhead + 1, "ring");
+    static_assert(kBuf == kAhead + 1 && kAhead <= 3, "ring");
 
     __shared__ __attribute__((aligned(1024))) unsigned char s_ring[kBuf][2 * HALF];
     __shared__ int s_idx[kSeg];
@@ -123,14 +135,6 @@ sparse_attn_kernel(AttnArgs a, int64_t row0, int64_t nrows)
 #pragma unroll
         for (int s = 0; s < KS; ++s) qop[s] = as_op(*reinterpret_cast<const u32x4_t *>(qr + 32 * s));
     }
-    // B operand of the transposition: identity over one 32-column block;
-    // lane (hh, col) holds rows 16s + 8hh + e of column col
-    bf16x8_t ident[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ident[s][e] = __bf16(16 * s + 8 * hh + e == col ? 1.f : 0.f);
-
     const unsigned char *kbase = a.k + b * a.T * int64_t(ROWB);
     const unsigned char *vbase = a.v + b * a.T * int64_t(ROWB);
     const int32_t *list = a.idx + row * int64_t(a.n_sel);
@@ -148,7 +152,9 @@ sparse_attn_kernel(AttnArgs a, int64_t row0, int64_t nrows)
     // tile `t` of the staged segment into ring buffer `buf`: this wave's
     // blocks j = wave + v*W; block j < NBLK/2 holds key rows, the rest value
     // rows; the lane's 16 bytes land at chunk p of row r and carry the row's
-    // logical chunk p ^ (r % NC).  Padding entries load row 0 (never used).
+    // logical chunk p ^ swizzle(r): r % NC for key rows (32 rows read at one
+    // chunk), 2r % NC for value rows (4 rows read at two adjacent chunks).
+    // Padding entries load row 0 (never used).
     auto dma_tile = [&](int t, int buf) {
 #pragma unroll
         for (int v = 0; v < BPW; ++v) {
@@ -158,8 +164,9 @@ sparse_attn_kernel(AttnArgs a, int64_t row0, int64_t nrows)
             const int r = off / ROWB;
             const int p = (off % ROWB) / 16;
             const int s = s_idx[t * KT + r];
+            const int swz = is_v ? (2 * r) % NC : r % NC;
             const unsigned char *src = (is_v ? vbase : kbase) +
-                                       int64_t(s >= 0 ? s : 0) * ROWB + 16 * (p ^ (r % NC));
+                                       int64_t(s >= 0 ? s : 0) * ROWB + 16 * (p ^ swz);
             __builtin_amdgcn_global_load_lds(
                 src, (__attribute__((address_space(3))) void *)&s_ring[buf][j * 1024], 16, 0, 0);
         }
@@ -179,22 +186,20 @@ sparse_attn_kernel(AttnArgs a, int64_t row0, int64_t nrows)
         for (int t = 0; t < kAhead && t < ntiles; ++t) dma_tile(t, t);
         for (int t = 0; t < ntiles; ++t) {
             const int buf = t % kBuf;
-            // this wave's loads of tile t done (those of tile t+1 may fly),
-            // then every wave's
-            if (t + 1 < ntiles)
-                __builtin_amdgcn_s_waitcnt(vm_wait_imm(BPW));
-            else
-                __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+            // this wave's loads of tile t done (later tiles may fly), then
+            // every wave's
+            wait_tiles<BPW>(ntiles - 1 - t < kAhead - 1 ? ntiles - 1 - t : kAhead - 1);
             __builtin_amdgcn_s_barrier();
             __asm__ volatile("" ::: "memory");
-            // every wave is past tile t-1: its buffer takes tile t+2
+            // every wave is past tile t-1: its buffer takes tile t+kAhead
             if (t + kAhead < ntiles) dma_tile(t + kAhead, (t + kAhead) % kBuf);
 
             const uint32_t vmask =
                 uint32_t(__builtin_amdgcn_ballot_w64(s_idx[t * KT + col] >= 0));  // bit = tile key
             if (vmask == 0) continue;
             const unsigned char *kt = &s_ring[buf][0];
-            const unsigned char *vt = &s_ring[buf][HALF];
+            __attribute__((address_space(3))) unsigned char *vt_lds =
+                (__attribute__((address_space(3))) unsigned char *)&s_ring[buf][HALF];
             const int swz = col % NC;
             // S^T[key][head] for the tile's 32 keys and the wave's 32 heads
             f32x16_t s0, s1;
@@ -236,25 +241,32 @@ sparse_attn_kernel(AttnArgs a, int64_t row0, int64_t nrows)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) acc[mb][i] *= alpha;
             }
+            // O^T[dv][head] += V^T[dv][keys] . P^T[keys][head].  The A operand
+            // (lane: column 32mb + col, keys 16j + 8rho + 4hh + 0..3 for
+            // rho = 0, 1) comes from two LDS transpose reads: in each group of
+            // 16 lanes, lane i receives element i % 4 of the 8 bytes addressed
+            // by lane 4e + i / 4, for e = 0..3; so lane g*16 + s points at
+            // key 16j + 8rho + 4hh + s/4, columns 32mb + 16(g%2) + 4(s%4) ..+3.
+            const int g16 = (lane >> 4) & 1;
+            const int s16 = lane & 15;
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                // V_tile[keys][32mb ..] . I: lane gets column 32mb + col at
-                // the keys of its score registers, exactly
-                f32x16_t tv;
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) tv[i] = 0.f;
+                for (int mb = 0; mb < MB; ++mb) {
+                    s4_t part[2];
 #pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    tv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        lds_op(vt + col * ROWB + 16 * ((4 * mb + 2 * s + hh) ^ swz)), ident[s], tv,
-                        0, 0, 0);
-                bf16x8_t va[2];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) va[i >> 3][i & 7] = __bf16(tv[i]);
-                // O^T[dv][head] += V^T[dv][keys] . P^T[keys][head]
-                acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[0], pb[0], acc[mb], 0, 0, 0);
-                acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[1], pb[1], acc[mb], 0, 0, 0);
-            }
+                    for (int rho = 0; rho < 2; ++rho) {
+                        const int key = 16 * j + 8 * rho + 4 * hh + (s16 >> 2);
+                        const int dv = 32 * mb + 16 * g16 + 4 * (s16 & 3);
+                        const int off = key * ROWB + 16 * ((dv >> 3) ^ ((2 * key) % NC)) + 2 * (dv & 7);
+                        part[rho] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) s4_t *)(vt_lds + off));
+                    }
+                    const bf16x8_t va = __builtin_bit_cast(
+                        bf16x8_t, s8_t{part[0][0], part[0][1], part[0][2], part[0][3],
+                                       part[1][0], part[1][1], part[1][2], part[1][3]});
+                    acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[j], acc[mb], 0, 0, 0);
+                }
         }
     }
 
