@@ -110,9 +110,9 @@ def cpu_baseline(inp, wl, nrows, seed=0):
                        f"fp64 scores + full sort, {dt:.1f} s")}
 
 
-ATTN_METRIC = "sparse attention over the selected keys, queries/sec at S=262K, 1 GPU"
-COMPOSITE_METRIC = "indexer + sparse attention step, queries/sec at S=262K, 1 GPU"
-INDEXER_FOR = {"attn-s256k": "s256k", "attn-s64k": "s64k"}
+ATTN_METRIC = "sparse attention over the selected keys, queries/sec, 1 GPU"
+COMPOSITE_METRIC = "indexer + sparse attention step, queries/sec, 1 GPU"
+INDEXER_FOR = {"attn-s256k": "s256k", "attn-s64k": "s64k", "attn-dec64": "dec64"}
 
 
 def attn_cpu_baseline(att, aw, nrows, seed=0):
@@ -155,12 +155,13 @@ def attention(csa, args):
     ind = None
     if args.composite:
         wl = WORKLOADS[INDEXER_FOR[aw.name]]
-        assert (wl.B, wl.S, wl.n_keys, wl.m, wl.k) == (aw.B, aw.S, aw.T, aw.m, aw.n_sel)
+        assert (wl.B, wl.S, wl.n_keys, wl.m, wl.k, wl.row_offset) == \
+            (aw.B, aw.S, aw.T, aw.m, aw.n_sel, aw.row_offset)
         del att["idx"]  # the indexer's lists replace the seeded ones
         ind = make_inputs(wl, seed=0, device=dev)
         idx = torch.empty((wl.B, wl.S, wl.k), dtype=torch.int32, device=dev)
         score = torch.empty((wl.B, wl.S, wl.k), dtype=torch.float32, device=dev)
-        ws = csa.workspace_for(ind["q"], ind["k"], wl.m, wl.k)
+        ws = csa.workspace_for(ind["q"], ind["k"], wl.m, wl.k, row_offset=wl.row_offset)
     else:
         idx = att["idx"]
     out = torch.empty((aw.B, aw.S, aw.H, aw.D), dtype=torch.bfloat16, device=dev)
@@ -170,7 +171,7 @@ def attention(csa, args):
     def step(i=None):
         if ind is not None:
             csa.index(ind["q"], ind["w"], ind["k"], wl.m, wl.k, out_idx=idx, out_score=score,
-                      workspace=ws, stream=stream)
+                      row_offset=wl.row_offset, workspace=ws, stream=stream)
         if i is not None:
             events.record(events.pairs[i][0], stream)
         csa.sparse_attention(att["q"], att["k"], att["v"], idx, aw.softmax_scale, out=out,
@@ -212,7 +213,8 @@ def attention(csa, args):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": aw.name, "B": aw.B, "S": aw.S, "T": aw.T, "H": aw.H, "D": aw.D,
-                   "n_sel": aw.n_sel, "m": aw.m, "lists": "indexer" if ind is not None else
+                   "n_sel": aw.n_sel, "m": aw.m, "row_offset": aw.row_offset,
+                   "lists": "indexer" if ind is not None else
                    "seeded", "scale": aw.softmax_scale},
         "attention_kernel_ms": kernel_avg,
         "attended_entries": entries,

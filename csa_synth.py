@@ -237,6 +237,9 @@ ATTN_WORKLOADS = {
     "attn-s256k": AttnWorkload("attn-s256k", B=1, S=262144, T=65536, H=64, D=128, n_sel=2048),
     "attn-s64k": AttnWorkload("attn-s64k", B=1, S=65536, T=16384, H=64, D=128, n_sel=2048),
     "attn-small": AttnWorkload("attn-small", B=2, S=700, T=175, H=64, D=128, n_sel=100),
+    # 64 positions at the end of a 262,144-position context (a decode step)
+    "attn-dec64": AttnWorkload("attn-dec64", B=1, S=64, T=65536, H=64, D=128, n_sel=2048,
+                               row_offset=262080),
 }
 
 _AFFINE_P = 2_147_483_647  # prime: invertible modulo every visible count below it

@@ -79,28 +79,12 @@ __device__ __forceinline__ float pair_sum(float x)
 // no LDS / scalar access outstanding (lgkmcnt 0), export count untouched.
 constexpr int vm_wait_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4); }
 
-constexpr int kSeg = 1024;  // index-list entries staged in LDS at a time
-constexpr int kBuf = 2;     // LDS ring of key/value tiles (36 KB: four workgroups per CU)
-constexpr int kAhead = 1;   // tiles in flight ahead of the one being computed
-
-// Waits until this wave has at most `later` tiles of BPW loads in flight.
-template <int BPW>
-__device__ __forceinline__ void wait_tiles(int later)
-{
-    if (later >= 2)
-        __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * BPW));
-    else if (later == 1)
-        __builtin_amdgcn_s_waitcnt(vm_wait_imm(BPW));
-    else
-        __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
-}
 
 template <int H, int D>
 __global__ void __launch_bounds__(64 * (H / 32))
 sparse_attn_kernel(AttnArgs a, int64_t row0, int64_t nrows)
 {
     constexpr int W = H / 32;              // waves; wave w owns heads 32w .. 32w+31
-    constexpr int NT = 64 * W;
     constexpr int ROWB = 2 * D;            // bytes of one key or value row
     constexpr int NC = ROWB / 16;          // 16-byte chunks per row
     constexpr int HALF = KT * ROWB;        // bytes of the tile's key (or value) rows
@@ -109,10 +93,9 @@ sparse_attn_kernel(AttnArgs a, int64_t row0, int64_t nrows)
     constexpr int KS = D / 16;             // K steps of the score product
     constexpr int MB = D / 32;             // 32-row blocks of the output
     static_assert(NBLK % W == 0 && BPW <= 32, "DMA layout");
-    static_assert(kBuf == kAhead + 1 && kAhead <= 3, "ring");
 
-    __shared__ __attribute__((aligned(1024))) unsigned char s_ring[kBuf][2 * HALF];
-    __shared__ int s_idx[kSeg];
+    // two tile buffers: the one being computed and the one being loaded
+    __shared__ __attribute__((aligned(1024))) unsigned char s_ring[2][2 * HALF];
 
     // consecutive rows on one XCD: workgroup i runs on XCD i % 8
     const int64_t per_xcd = (nrows + kXcds - 1) / kXcds;
@@ -139,6 +122,8 @@ sparse_attn_kernel(AttnArgs a, int64_t row0, int64_t nrows)
     const unsigned char *vbase = a.v + b * a.T * int64_t(ROWB);
     const int32_t *list = a.idx + row * int64_t(a.n_sel);
     const int64_t T = a.T;
+    const int n_sel = a.n_sel;
+    const int ntiles = T > 0 ? (n_sel + KT - 1) / KT : 0;
 
     f32x16_t acc[MB];
 #pragma unroll
@@ -149,13 +134,21 @@ sparse_attn_kernel(AttnArgs a, int64_t row0, int64_t nrows)
     float l_run = 0.f;        // this lane's part of the running sum of weights
     const float c = a.scale * kLog2e;
 
-    // tile `t` of the staged segment into ring buffer `buf`: this wave's
-    // blocks j = wave + v*W; block j < NBLK/2 holds key rows, the rest value
-    // rows; the lane's 16 bytes land at chunk p of row r and carry the row's
-    // logical chunk p ^ swizzle(r): r % NC for key rows (32 rows read at one
-    // chunk), 2r % NC for value rows (4 rows read at two adjacent chunks).
-    // Padding entries load row 0 (never used).
-    auto dma_tile = [&](int t, int buf) {
+    // Entry `col` of tile t (a key index in [0, T), or -1): every lane
+    // loads one, so lanes r and r + 32 hold entry r of the tile.
+    auto load_entry = [&](int t) -> int {
+        const int pos = t * KT + col;
+        if (t >= ntiles || pos >= n_sel) return -1;
+        const int s = list[pos];
+        return (s >= 0 && s < T) ? s : -1;
+    };
+    // One tile into buffer `buf`, given the lane's entry `ent` of it: this
+    // wave's blocks j = wave + v*W; block j < NBLK/2 holds key rows, the
+    // rest value rows; the lane's 16 bytes land at chunk p of row r and carry
+    // the row's logical chunk p ^ swizzle(r): r % NC for key rows (32 rows
+    // read at one chunk), 2r % NC for value rows (4 rows read at two adjacent
+    // chunks).  Padding entries load row 0 (never used).
+    auto dma_tile = [&](int ent, int buf) {
 #pragma unroll
         for (int v = 0; v < BPW; ++v) {
             const int j = wave + v * W;
@@ -163,7 +156,7 @@ sparse_attn_kernel(AttnArgs a, int64_t row0, int64_t nrows)
             const int off = (is_v ? j - NBLK / 2 : j) * 1024 + lane * 16;
             const int r = off / ROWB;
             const int p = (off % ROWB) / 16;
-            const int s = s_idx[t * KT + r];
+            const int s = __shfl(ent, r);
             const int swz = is_v ? (2 * r) % NC : r % NC;
             const unsigned char *src = (is_v ? vbase : kbase) +
                                        int64_t(s >= 0 ? s : 0) * ROWB + 16 * (p ^ swz);
@@ -172,30 +165,27 @@ sparse_attn_kernel(AttnArgs a, int64_t row0, int64_t nrows)
         }
     };
 
-    for (int seg0 = 0; seg0 < a.n_sel && T > 0; seg0 += kSeg) {
-        const int nseg = a.n_sel - seg0 < kSeg ? a.n_sel - seg0 : kSeg;
-        const int ntiles = (nseg + KT - 1) / KT;
-        __syncthreads();  // the previous segment is done with s_idx and the ring
-        for (int i = tid; i < ntiles * KT; i += NT) {
-            const int s = i < nseg ? list[seg0 + i] : -1;
-            s_idx[i] = (s >= 0 && s < T) ? s : -1;
+    {
+        int e_cur = load_entry(0);   // the lane's entry of the tile being computed
+        int e_next = load_entry(1);  // ... of the next tile
+        if (ntiles > 0) {
+            __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+            dma_tile(e_cur, 0);
         }
-        __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));  // nothing but tile loads in flight below
-        __syncthreads();
-
-        for (int t = 0; t < kAhead && t < ntiles; ++t) dma_tile(t, t);
         for (int t = 0; t < ntiles; ++t) {
-            const int buf = t % kBuf;
-            // this wave's loads of tile t done (later tiles may fly), then
-            // every wave's
-            wait_tiles<BPW>(ntiles - 1 - t < kAhead - 1 ? ntiles - 1 - t : kAhead - 1);
+            const int buf = t & 1;
+            // this wave's loads are done (tile t and the entries of tile
+            // t + 1), then every wave's
+            __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
             __builtin_amdgcn_s_barrier();
             __asm__ volatile("" ::: "memory");
-            // every wave is past tile t-1: its buffer takes tile t+kAhead
-            if (t + kAhead < ntiles) dma_tile(t + kAhead, (t + kAhead) % kBuf);
+            // every wave is past tile t-1: its buffer takes tile t+1
+            if (t + 1 < ntiles) dma_tile(e_next, buf ^ 1);
+            const int ent = e_cur;
+            e_cur = e_next;
+            e_next = load_entry(t + 2);  // lands before the next wait
 
-            const uint32_t vmask =
-                uint32_t(__builtin_amdgcn_ballot_w64(s_idx[t * KT + col] >= 0));  // bit = tile key
+            const uint32_t vmask = uint32_t(__builtin_amdgcn_ballot_w64(ent >= 0));  // bit = tile key
             if (vmask == 0) continue;
             const unsigned char *kt = &s_ring[buf][0];
             __attribute__((address_space(3))) unsigned char *vt_lds =
