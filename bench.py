@@ -166,6 +166,10 @@ def attention(csa, args):
         idx = att["idx"]
     out = torch.empty((aw.B, aw.S, aw.H, aw.D), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((aw.B, aw.S, aw.H), dtype=torch.float32, device=dev)
+    splits = args.entry_splits
+    G, _ = csa.attention_plan(csa.make_attn_desc(aw.B, aw.S, aw.T, aw.H, aw.D, aw.n_sel),
+                              csa.make_attn_options(splits))
+    aws = csa.attention_workspace_for(att["q"], att["k"], aw.n_sel, splits)
     events = csa.HipEvents(args.steps)
 
     def step(i=None):
@@ -175,7 +179,7 @@ def attention(csa, args):
         if i is not None:
             events.record(events.pairs[i][0], stream)
         csa.sparse_attention(att["q"], att["k"], att["v"], idx, aw.softmax_scale, out=out,
-                             lse=lse, stream=stream)
+                             lse=lse, entry_splits=splits, workspace=aws, stream=stream)
         if i is not None:
             events.record(events.pairs[i][1], stream)
 
@@ -214,6 +218,7 @@ def attention(csa, args):
         "data": "synthetic",
         "config": {"workload": aw.name, "B": aw.B, "S": aw.S, "T": aw.T, "H": aw.H, "D": aw.D,
                    "n_sel": aw.n_sel, "m": aw.m, "row_offset": aw.row_offset,
+                   "entry_splits": G,
                    "lists": "indexer" if ind is not None else
                    "seeded", "scale": aw.softmax_scale},
         "attention_kernel_ms": kernel_avg,
@@ -292,6 +297,9 @@ def main():
                     help="time the five chunk sizes (k=2048) and the five top-k values "
                          "(default chunk) on the S=65,536 workload, one JSON line per cell; "
                          "the GPU tests check every cell against the oracle")
+    ap.add_argument("--entry-splits", type=int, default=0,
+                    help="with an attn-* workload: ranges per row of the attention (0 = "
+                         "automatic, 1 = none)")
     ap.add_argument("--composite", action="store_true",
                     help="with an attn-* workload: run the indexer before the attention "
                          "each step and attend over its lists")

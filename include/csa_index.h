@@ -219,12 +219,53 @@ typedef struct {
  * csa_sparse_attention: softmax attention of every query row over the
  * entries its index list selects (see above).  `scale` multiplies q.k (for
  * example 1/sqrt(D)) and must be finite.  Writes only out and lse.  No
- * device memory is allocated.  Deterministic: bitwise identical across runs.
+ * device memory is allocated and rows are never split (entry_splits = 1).
+ * Deterministic: bitwise identical across runs.
  * Returns CSA_OK or a negative csa_status; on error nothing is launched.
  */
 int csa_sparse_attention(const void *q, const void *k, const void *v,
                          const int32_t *idx, const csa_attn_desc *desc,
                          float scale, void *out, float *lse, hipStream_t stream);
+
+/*
+ * Optional controls of csa_sparse_attention_ex (NULL = all defaults).
+ *   entry_splits  Ranges each row's index list is split into, each handled by
+ *                 its own workgroup, with a combine pass after (for short
+ *                 query blocks such as a decode step, where rows alone leave
+ *                 the device idle).  0 = automatic: 1 while B*S rows reach
+ *                 four workgroups per compute unit, otherwise enough ranges
+ *                 of at least 512 entries to get there.  1 = no split (the
+ *                 plain csa_sparse_attention).  n > 1 asks for n ranges (at
+ *                 most one per 32 entries).  Ranges change rounding only:
+ *                 results stay within the documented bound, and are
+ *                 deterministic for a given count.
+ *   num_cus       Compute units to plan for; 0 = ask the current device.
+ *   workspace     Device scratch of workspace_bytes bytes (256-byte aligned)
+ *                 for the ranges' partial results, B*S*G*H*(D+2)*4 bytes;
+ *                 NULL = the library allocates it stream-ordered
+ *                 (hipMallocAsync / hipFreeAsync on `stream`) when G > 1.
+ *   reserved      Must be 0.
+ */
+typedef struct {
+    int32_t entry_splits;
+    int32_t num_cus;
+    void *workspace;
+    size_t workspace_bytes;
+    int64_t reserved;
+} csa_attn_options;
+
+/* csa_sparse_attention with explicit options (see csa_attn_options). */
+int csa_sparse_attention_ex(const void *q, const void *k, const void *v,
+                            const int32_t *idx, const csa_attn_desc *desc,
+                            float scale, void *out, float *lse,
+                            const csa_attn_options *opt, hipStream_t stream);
+
+/* Device scratch bytes csa_sparse_attention_ex needs for these arguments
+ * (0 when the rows are not split, and on invalid arguments).  The split
+ * count it implies is written to *entry_splits when that is not NULL. */
+size_t csa_sparse_attention_workspace_bytes(const csa_attn_desc *desc,
+                                            const csa_attn_options *opt,
+                                            int32_t *entry_splits);
 
 #ifdef __cplusplus
 }

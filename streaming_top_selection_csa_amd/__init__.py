@@ -6,10 +6,12 @@ the C ABI in include/csa_index.h); this package is its Python binding.
 Importing it loads nothing; the library is loaded on first use and calls
 fail loudly if it is missing.
 """
-from .binding import (CSA_BF16, CSA_FP8_E4M3FN, CsaError, HipEvents, index, load_library,
-                      make_attn_desc, make_desc, make_options, plan_query, sparse_attention,
+from .binding import (CSA_BF16, CSA_FP8_E4M3FN, CsaError, HipEvents, attention_plan,
+                      attention_workspace_for, index, load_library, make_attn_desc,
+                      make_attn_options, make_desc, make_options, plan_query, sparse_attention,
                       status_string, workspace_bytes, workspace_for)
 
-__all__ = ["index", "sparse_attention", "make_attn_desc", "plan_query", "workspace_bytes", "workspace_for", "load_library",
+__all__ = ["index", "sparse_attention", "make_attn_desc", "make_attn_options", "attention_plan",
+           "attention_workspace_for", "plan_query", "workspace_bytes", "workspace_for", "load_library",
            "status_string", "make_desc", "make_options", "CsaError", "HipEvents",
            "CSA_BF16", "CSA_FP8_E4M3FN"]

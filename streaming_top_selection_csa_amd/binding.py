@@ -28,7 +28,8 @@ CSA_BF16 = 0
 CSA_FP8_E4M3FN = 1
 
 EXPORTS = ("csa_index", "csa_index_ex", "csa_workspace_bytes", "csa_plan_query",
-           "csa_status_string", "csa_sparse_attention")
+           "csa_status_string", "csa_sparse_attention", "csa_sparse_attention_ex",
+           "csa_sparse_attention_workspace_bytes")
 
 
 class CsaDesc(ctypes.Structure):
@@ -56,6 +57,12 @@ class CsaAttnDesc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("S", ctypes.c_int64), ("T", ctypes.c_int64),
                 ("H", ctypes.c_int32), ("D", ctypes.c_int32), ("n_sel", ctypes.c_int32),
                 ("reserved0", ctypes.c_int32)]
+
+
+class CsaAttnOptions(ctypes.Structure):
+    _fields_ = [("entry_splits", ctypes.c_int32), ("num_cus", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("reserved", ctypes.c_int64)]
 
 
 class CsaError(RuntimeError):
@@ -91,6 +98,13 @@ def load_library():
     lib.csa_sparse_attention.argtypes = [vp, vp, vp, vp, ctypes.POINTER(CsaAttnDesc),
                                          ctypes.c_float, vp, vp, vp]
     lib.csa_sparse_attention.restype = ctypes.c_int
+    lib.csa_sparse_attention_ex.argtypes = [vp, vp, vp, vp, ctypes.POINTER(CsaAttnDesc),
+                                            ctypes.c_float, vp, vp,
+                                            ctypes.POINTER(CsaAttnOptions), vp]
+    lib.csa_sparse_attention_ex.restype = ctypes.c_int
+    lib.csa_sparse_attention_workspace_bytes.argtypes = [
+        ctypes.POINTER(CsaAttnDesc), ctypes.POINTER(CsaAttnOptions), ctypes.POINTER(ctypes.c_int32)]
+    lib.csa_sparse_attention_workspace_bytes.restype = ctypes.c_size_t
     lib.csa_status_string.argtypes = [ctypes.c_int]
     lib.csa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -217,16 +231,42 @@ def make_attn_desc(B, S, T, H, D, n_sel) -> CsaAttnDesc:
     return CsaAttnDesc(int(B), int(S), int(T), int(H), int(D), int(n_sel), 0)
 
 
+def make_attn_options(entry_splits=1, num_cus=0, workspace=None, workspace_bytes=0):
+    return CsaAttnOptions(int(entry_splits), int(num_cus), workspace, int(workspace_bytes), 0)
+
+
+def attention_plan(desc: CsaAttnDesc, opt: Optional[CsaAttnOptions] = None):
+    """(entry_splits, workspace bytes) csa_sparse_attention_ex would use."""
+    g = ctypes.c_int32(0)
+    n = load_library().csa_sparse_attention_workspace_bytes(
+        ctypes.byref(desc), ctypes.byref(opt) if opt is not None else None, ctypes.byref(g))
+    return int(g.value), int(n)
+
+
+def attention_workspace_for(q: torch.Tensor, k: torch.Tensor, n_sel: int,
+                            entry_splits: int = 0) -> torch.Tensor:
+    """A torch-allocated workspace big enough for `sparse_attention` with
+    this split setting (empty when the rows are not split)."""
+    B, S, H, D = q.shape
+    _, n = attention_plan(make_attn_desc(B, S, k.shape[1], H, D, n_sel),
+                          make_attn_options(entry_splits))
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+
+
 def sparse_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
                      scale: Optional[float] = None, *, out: Optional[torch.Tensor] = None,
                      lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+                     entry_splits: int = 1, workspace: Optional[torch.Tensor] = None,
                      stream: Optional[torch.cuda.Stream] = None):
     """Softmax attention of every query row over its selected compressed
-    entries (csa_sparse_attention).
+    entries (csa_sparse_attention_ex).
 
     q [B,S,H,D] bf16, k and v [B,T,D] bf16, idx [B,S,n_sel] int32 (entries
     outside [0, T) are padding; csa_index's out_idx fits).  `scale`
-    multiplies q.k (default 1/sqrt(D)).  Returns (out bf16 [B,S,H,D],
+    multiplies q.k (default 1/sqrt(D)).  `entry_splits`: 1 = one workgroup
+    per row (no workspace), 0 = automatic ranges for short query blocks,
+    n = n ranges per row; `workspace` holds their partial results (else the
+    library allocates it stream-ordered).  Returns (out bf16 [B,S,H,D],
     lse fp32 [B,S,H] or None).  Asynchronous on `stream`.
     """
     lib = load_library()
@@ -253,14 +293,19 @@ def sparse_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: tor
         if tuple(lse.shape) != (B, S, H):
             raise ValueError("lse must be [B,S,H]")
     desc = make_attn_desc(B, S, T, H, D, idx.shape[2])
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _check(workspace, "workspace")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    opt = make_attn_options(entry_splits, 0, ws_ptr, ws_bytes)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    rc = lib.csa_sparse_attention(q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(),
-                                  ctypes.byref(desc), float(scale), out.data_ptr(),
-                                  lse.data_ptr() if lse is not None else None,
-                                  ctypes.c_void_p(stream.cuda_stream))
+    rc = lib.csa_sparse_attention_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(),
+                                     ctypes.byref(desc), float(scale), out.data_ptr(),
+                                     lse.data_ptr() if lse is not None else None,
+                                     ctypes.byref(opt), ctypes.c_void_p(stream.cuda_stream))
     if rc != CSA_OK:
-        raise CsaError(rc, "csa_sparse_attention")
+        raise CsaError(rc, "csa_sparse_attention_ex")
     return out, lse
 
 

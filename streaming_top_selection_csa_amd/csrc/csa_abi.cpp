@@ -164,15 +164,25 @@ extern "C" int csa_index(const void *q, const float *w, const void *k_cmp,
     return csa_index_ex(q, w, k_cmp, desc, m, k, out_idx, out_score, nullptr, stream);
 }
 
-extern "C" int csa_sparse_attention(const void *q, const void *k, const void *v,
-                                    const int32_t *idx, const csa_attn_desc *desc, float scale,
-                                    void *out, float *lse, hipStream_t stream)
+namespace {
+
+struct AttnPlan {
+    int64_t rows = 0;
+    int splits = 1;
+    int split_entries = 0;
+    size_t ws_bytes = 0;
+};
+
+constexpr int kAttnTile = 32;         // entries per tile of the attention kernel
+constexpr int kAttnMinRangeTiles = 16; // automatic ranges hold at least 512 entries
+constexpr int kAttnUnitsPerCu = 4;    // workgroups per compute unit the split aims for
+
+int attn_plan(const csa_attn_desc *desc, const csa_attn_options *opt, AttnPlan *p)
 {
     if (!desc) return CSA_ERR_INVALID_ARG;
     const csa_attn_desc &d = *desc;
     if (d.B < 1 || d.S < 0 || d.T < 0 || d.n_sel < 0 || d.reserved0 != 0)
         return CSA_ERR_INVALID_ARG;
-    if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return CSA_ERR_INVALID_ARG;
     if (!((d.H == 32 || d.H == 64 || d.H == 128) && (d.D == 64 || d.D == 128)))
         return CSA_ERR_UNSUPPORTED;
     // element counts must stay addressable with 64-bit byte offsets
@@ -182,12 +192,83 @@ extern "C" int csa_sparse_attention(const void *q, const void *k, const void *v,
     if (rows > kMaxElems / (int64_t(d.H) * d.D) || (d.n_sel > 0 && rows > kMaxElems / d.n_sel) ||
         d.B * d.T > kMaxElems / d.D)
         return CSA_ERR_INVALID_ARG;
-    if (rows == 0) return CSA_OK;
+    if (opt && (opt->entry_splits < 0 || opt->num_cus < 0 || opt->reserved != 0))
+        return CSA_ERR_INVALID_ARG;
+    p->rows = rows;
+    p->splits = 1;
+    p->split_entries = d.n_sel;
+    p->ws_bytes = 0;
+    const int tiles = (d.n_sel + kAttnTile - 1) / kAttnTile;
+    const int req = opt ? opt->entry_splits : 1;
+    if (rows == 0 || d.T == 0 || tiles <= 1 || req == 1) return CSA_OK;
+    int G = 1;
+    if (req > 1) {
+        G = req < tiles ? req : tiles;
+    } else {
+        int cus = opt && opt->num_cus > 0 ? opt->num_cus : 0;
+        if (cus == 0) {
+            const int rc = device_cus(&cus);
+            if (rc != CSA_OK) return rc;
+        }
+        const int64_t target = int64_t(kAttnUnitsPerCu) * cus;
+        if (rows >= target) return CSA_OK;
+        const int64_t want = (target + rows - 1) / rows;
+        const int cap = tiles / kAttnMinRangeTiles > 1 ? tiles / kAttnMinRangeTiles : 1;
+        G = want < cap ? int(want) : cap;
+    }
+    if (G <= 1) return CSA_OK;
+    const int range_tiles = (tiles + G - 1) / G;
+    G = (tiles + range_tiles - 1) / range_tiles;  // no empty trailing range
+    if (G <= 1) return CSA_OK;
+    if (double(rows) * G * d.H * (d.D + 2) * 4.0 > double(int64_t(1) << 56))
+        return CSA_ERR_INVALID_ARG;  // partial results beyond any device
+    p->splits = G;
+    p->split_entries = range_tiles * kAttnTile;
+    p->ws_bytes = size_t(rows) * size_t(G) * size_t(d.H) * size_t(d.D + 2) * 4u;
+    return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" size_t csa_sparse_attention_workspace_bytes(const csa_attn_desc *desc,
+                                                       const csa_attn_options *opt,
+                                                       int32_t *entry_splits)
+{
+    AttnPlan p;
+    if (attn_plan(desc, opt, &p) != CSA_OK) return 0;
+    if (entry_splits) *entry_splits = p.splits;
+    return p.ws_bytes;
+}
+
+extern "C" int csa_sparse_attention_ex(const void *q, const void *k, const void *v,
+                                       const int32_t *idx, const csa_attn_desc *desc, float scale,
+                                       void *out, float *lse, const csa_attn_options *opt,
+                                       hipStream_t stream)
+{
+    AttnPlan p;
+    int rc = attn_plan(desc, opt, &p);
+    if (rc != CSA_OK) return rc;
+    const csa_attn_desc &d = *desc;
+    if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return CSA_ERR_INVALID_ARG;
+    if (p.rows == 0) return CSA_OK;
     if (!q || !out || (d.n_sel > 0 && !idx) || (d.T > 0 && (!k || !v)))
         return CSA_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
         !aligned(idx, 4) || !aligned(lse, 4))
         return CSA_ERR_INVALID_ARG;
+
+    void *ws = nullptr;
+    bool owned = false;
+    if (p.ws_bytes > 0) {
+        if (opt && opt->workspace) {
+            if (opt->workspace_bytes < p.ws_bytes || !aligned(opt->workspace, 256))
+                return CSA_ERR_WORKSPACE;
+            ws = opt->workspace;
+        } else {
+            if (hipMallocAsync(&ws, p.ws_bytes, stream) != hipSuccess) return CSA_ERR_HIP;
+            owned = true;
+        }
+    }
 
     csa::AttnArgs a;
     a.q = static_cast<const unsigned char *>(q);
@@ -201,5 +282,20 @@ extern "C" int csa_sparse_attention(const void *q, const void *k, const void *v,
     a.T = d.T;
     a.n_sel = d.n_sel;
     a.scale = scale;
-    return csa::launch_sparse_attention(a, d.H, d.D, stream) == hipSuccess ? CSA_OK : CSA_ERR_HIP;
+    a.n_splits = p.splits;
+    a.split_entries = p.split_entries;
+    a.part_o = static_cast<float *>(ws);
+    a.part_ml = p.ws_bytes > 0
+        ? static_cast<float *>(ws) + size_t(p.rows) * size_t(p.splits) * size_t(d.H) * size_t(d.D)
+        : nullptr;
+    rc = csa::launch_sparse_attention(a, d.H, d.D, stream) == hipSuccess ? CSA_OK : CSA_ERR_HIP;
+    if (owned && hipFreeAsync(ws, stream) != hipSuccess && rc == CSA_OK) rc = CSA_ERR_HIP;
+    return rc;
+}
+
+extern "C" int csa_sparse_attention(const void *q, const void *k, const void *v,
+                                    const int32_t *idx, const csa_attn_desc *desc, float scale,
+                                    void *out, float *lse, hipStream_t stream)
+{
+    return csa_sparse_attention_ex(q, k, v, idx, desc, scale, out, lse, nullptr, stream);
 }

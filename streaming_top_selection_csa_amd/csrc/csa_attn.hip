@@ -9,11 +9,12 @@
 // the compressed key and value rows.
 //
 // One workgroup per query row, one wave per 32 heads.  The row's index list
-// is staged in LDS (1,024 entries at a time); its entries are taken 32 at a
-// time (a tile).  Every tile's 32 key rows and 32 value rows stream from
-// global memory straight into LDS (global_load_lds, 16 bytes per lane) into a
-// ring of two buffers, one tile ahead; at 36 KB of LDS four workgroups share
-// a CU (more resident waves beat deeper rings here).  Each row's 16-byte
+// is taken 32 entries at a time (a tile); each lane loads one entry per
+// tile, one tile early.  Every tile's 32 key rows and 32 value rows stream
+// from global memory straight into LDS (global_load_lds, 16 bytes per lane)
+// into a ring of two buffers, one tile ahead; at 32 KB of LDS the register
+// budget (two waves per SIMD) is what bounds residency, four workgroups per
+// CU (more resident waves beat deeper rings here).  Each row's 16-byte
 // chunks are XOR-swizzled by row, so the operand reads below hit distinct
 // LDS banks.  For every tile each wave
 //   * computes the 32x32 block S^T = K_tile . Q^T of (key, head) scores with
@@ -41,6 +42,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 typedef short s4_t __attribute__((ext_vector_type(4)));
@@ -80,9 +82,14 @@ __device__ __forceinline__ float pair_sum(float x)
 constexpr int vm_wait_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4); }
 
 
-template <int H, int D>
+// One unit is a query row (SPLIT = false) or one of the n_splits ranges of
+// split_entries entries of a row's list (SPLIT = true: short query blocks,
+// where rows alone cannot fill the device).  A range writes its unnormalised
+// output, running maximum and weight sum to the partial buffers; the
+// combine kernel merges the ranges of a row.
+template <int H, int D, bool SPLIT>
 __global__ void __launch_bounds__(64 * (H / 32))
-sparse_attn_kernel(AttnArgs a, int64_t row0, int64_t nrows)
+sparse_attn_kernel(AttnArgs a, int64_t unit0, int64_t nunits)
 {
     constexpr int W = H / 32;              // waves; wave w owns heads 32w .. 32w+31
     constexpr int ROWB = 2 * D;            // bytes of one key or value row
@@ -97,11 +104,12 @@ sparse_attn_kernel(AttnArgs a, int64_t row0, int64_t nrows)
     // two tile buffers: the one being computed and the one being loaded
     __shared__ __attribute__((aligned(1024))) unsigned char s_ring[2][2 * HALF];
 
-    // consecutive rows on one XCD: workgroup i runs on XCD i % 8
-    const int64_t per_xcd = (nrows + kXcds - 1) / kXcds;
+    // consecutive units on one XCD: workgroup i runs on XCD i % 8
+    const int64_t per_xcd = (nunits + kXcds - 1) / kXcds;
     const int64_t slot = int64_t(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-    if (slot >= nrows) return;  // whole workgroup, before any barrier
-    const int64_t row = row0 + slot;
+    if (slot >= nunits) return;  // whole workgroup, before any barrier
+    const int64_t unit = unit0 + slot;
+    const int64_t row = SPLIT ? unit / a.n_splits : unit;
     const int64_t b = row / a.S;
 
     const int tid = threadIdx.x;
@@ -122,8 +130,11 @@ sparse_attn_kernel(AttnArgs a, int64_t row0, int64_t nrows)
     const unsigned char *vbase = a.v + b * a.T * int64_t(ROWB);
     const int32_t *list = a.idx + row * int64_t(a.n_sel);
     const int64_t T = a.T;
-    const int n_sel = a.n_sel;
-    const int ntiles = T > 0 ? (n_sel + KT - 1) / KT : 0;
+    // this unit's entries [e0, e1) of the row's list
+    const int e0 = SPLIT ? int(unit % a.n_splits) * a.split_entries : 0;
+    const int e1 = SPLIT ? (a.n_sel - e0 < a.split_entries ? a.n_sel : e0 + a.split_entries)
+                         : a.n_sel;
+    const int ntiles = (T > 0 && e1 > e0) ? (e1 - e0 + KT - 1) / KT : 0;
 
     f32x16_t acc[MB];
 #pragma unroll
@@ -137,8 +148,8 @@ sparse_attn_kernel(AttnArgs a, int64_t row0, int64_t nrows)
     // Entry `col` of tile t (a key index in [0, T), or -1): every lane
     // loads one, so lanes r and r + 32 hold entry r of the tile.
     auto load_entry = [&](int t) -> int {
-        const int pos = t * KT + col;
-        if (t >= ntiles || pos >= n_sel) return -1;
+        const int pos = e0 + t * KT + col;
+        if (t >= ntiles || pos >= e1) return -1;
         const int s = list[pos];
         return (s >= 0 && s < T) ? s : -1;
     };
@@ -262,6 +273,20 @@ sparse_attn_kernel(AttnArgs a, int64_t row0, int64_t nrows)
 
     // epilogue: lane holds head `col`, rows dv = 32mb + 8(i/4) + 4hh + i%4
     const float l_tot = pair_sum(l_run);
+    if constexpr (SPLIT) {
+        float *po = a.part_o + (unit * H + head) * int64_t(D);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<f32x4_t *>(po + 32 * mb + 8 * g + 4 * hh) =
+                    f32x4_t{acc[mb][4 * g], acc[mb][4 * g + 1], acc[mb][4 * g + 2], acc[mb][4 * g + 3]};
+        if (hh == 0) {
+            a.part_ml[(unit * H + head) * 2] = m_run;  // -inf for a range without entries
+            a.part_ml[(unit * H + head) * 2 + 1] = l_tot;
+        }
+        return;
+    }
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     unsigned char *orow = a.out + (row * H + head) * int64_t(ROWB);
 #pragma unroll
@@ -278,17 +303,67 @@ sparse_attn_kernel(AttnArgs a, int64_t row0, int64_t nrows)
         a.lse[row * H + head] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
+// Merges the n_splits ranges of each row: with M = max_g m_g (log2 units),
+// out = sum_g 2^(m_g - M) O_g / sum_g 2^(m_g - M) l_g, in range order.
+// 256 threads per row, four output columns each.
+template <int H, int D>
+__global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a, int64_t row0, int64_t nrows)
+{
+    const int64_t row = row0 + blockIdx.x;
+    if (blockIdx.x >= nrows) return;
+    const int G = a.n_splits;
+    for (int w = threadIdx.x; w < H * D / 4; w += 256) {
+        const int h = (4 * w) / D;
+        const int dv = (4 * w) % D;
+        const float *ml = a.part_ml + (row * G * H + h) * 2;  // range g at + g * 2H
+        float M = -INFINITY;
+        for (int g = 0; g < G; ++g) M = fmaxf(M, ml[g * 2 * H]);
+        f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+        float L = 0.f;
+        if (M != -INFINITY) {
+            for (int g = 0; g < G; ++g) {
+                const float sc = __builtin_amdgcn_exp2f(ml[g * 2 * H] - M);
+                L += sc * ml[g * 2 * H + 1];
+                const f32x4_t og = *reinterpret_cast<const f32x4_t *>(
+                    a.part_o + ((row * G + g) * H + h) * int64_t(D) + dv);
+                o += sc * og;
+            }
+        }
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        bf16x4_t ob;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ob[e] = __bf16(o[e] * inv);
+        *reinterpret_cast<u32x2_t *>(a.out + ((row * H + h) * int64_t(D) + dv) * 2) =
+            __builtin_bit_cast(u32x2_t, ob);
+        if (a.lse && dv == 0) a.lse[row * H + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+    }
+}
+
 template <int H, int D>
 hipError_t launch_hd(const AttnArgs &a, hipStream_t stream)
 {
     const int64_t rows = a.B * a.S;
-    // at most 2^22 rows per launch keeps grid * block far below 2^32
-    constexpr int64_t kMaxRows = int64_t(1) << 22;
-    for (int64_t r0 = 0; r0 < rows; r0 += kMaxRows) {
-        const int64_t n = rows - r0 < kMaxRows ? rows - r0 : kMaxRows;
+    const bool split = a.n_splits > 1;
+    const int64_t units = split ? rows * a.n_splits : rows;
+    // at most 2^22 workgroups per launch keeps grid * block far below 2^32
+    constexpr int64_t kMaxUnits = int64_t(1) << 22;
+    for (int64_t u0 = 0; u0 < units; u0 += kMaxUnits) {
+        const int64_t n = units - u0 < kMaxUnits ? units - u0 : kMaxUnits;
         const int64_t grid = kXcds * ((n + kXcds - 1) / kXcds);
-        hipLaunchKernelGGL((sparse_attn_kernel<H, D>), dim3(unsigned(grid)), dim3(64 * (H / 32)),
-                           0, stream, a, r0, n);
+        if (split)
+            hipLaunchKernelGGL((sparse_attn_kernel<H, D, true>), dim3(unsigned(grid)),
+                               dim3(64 * (H / 32)), 0, stream, a, u0, n);
+        else
+            hipLaunchKernelGGL((sparse_attn_kernel<H, D, false>), dim3(unsigned(grid)),
+                               dim3(64 * (H / 32)), 0, stream, a, u0, n);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (!split) return hipSuccess;
+    for (int64_t r0 = 0; r0 < rows; r0 += kMaxUnits) {
+        const int64_t n = rows - r0 < kMaxUnits ? rows - r0 : kMaxUnits;
+        hipLaunchKernelGGL((attn_combine_kernel<H, D>), dim3(unsigned(n)), dim3(256), 0, stream,
+                           a, r0, n);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -51,6 +51,10 @@ struct AttnArgs {
     int64_t B, S, T;
     int n_sel;
     float scale;                // multiplies q . k
+    int n_splits;               // ranges per row (1: none)
+    int split_entries;          // entries per range (a multiple of 32)
+    float *part_o;              // [B*S*n_splits, H, D] unnormalised range outputs
+    float *part_ml;             // [B*S*n_splits, H, 2] range maximum (log2 units), weight sum
 };
 
 // H in {32, 64, 128}, D in {64, 128}; anything else is hipErrorInvalidValue.

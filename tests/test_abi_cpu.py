@@ -237,3 +237,48 @@ def test_sparse_attention_validation(lib):
     # nothing to do: no rows (no pointer is needed)
     assert attn_call(lib, csa.make_attn_desc(1, 0, 10, 64, 128, 8), q=0, k=0, v=0, idx=0,
                      out=0) == B.CSA_OK
+
+
+def attn_plan(desc, **kw):
+    kw.setdefault("num_cus", 256)
+    return csa.attention_plan(desc, csa.make_attn_options(**kw))
+
+
+def test_sparse_attention_split_plan(lib):
+    dec = csa.make_attn_desc(1, 64, 65536, 64, 128, 2048)
+    # 64 rows on 256 CUs: ranges of at least 512 entries toward 4 workgroups per CU
+    assert attn_plan(dec, entry_splits=0) == (4, 64 * 4 * 64 * 130 * 4)
+    assert attn_plan(dec, entry_splits=1) == (1, 0)
+    assert attn_plan(dec, entry_splits=5)[0] == 5            # 64 tiles -> ranges of 13 tiles
+    assert attn_plan(dec, entry_splits=100)[0] == 64         # at most one range per tile
+    assert attn_plan(dec, entry_splits=0, num_cus=8)[0] == 1  # 64 rows already fill 8 CUs
+    big = csa.make_attn_desc(1, 262144, 65536, 64, 128, 2048)
+    assert attn_plan(big, entry_splits=0) == (1, 0)
+    assert attn_plan(csa.make_attn_desc(1, 4, 100, 64, 128, 20), entry_splits=0)[0] == 1
+    assert attn_plan(csa.make_attn_desc(1, 4, 0, 64, 128, 2048), entry_splits=0)[0] == 1
+    # the workspace query writes the split count
+    g = ctypes.c_int32(-7)
+    n = lib.csa_sparse_attention_workspace_bytes(ctypes.byref(dec), ctypes.byref(
+        csa.make_attn_options(3, 256)), ctypes.byref(g))
+    assert g.value == 3 and n == 64 * 3 * 64 * 130 * 4
+
+
+def test_sparse_attention_ex_validation(lib):
+    E = B.CSA_ERR_INVALID_ARG
+    dec = csa.make_attn_desc(1, 64, 65536, 64, 128, 2048)
+    vp = ctypes.c_void_p
+
+    def call(opt):
+        return lib.csa_sparse_attention_ex(vp(16), vp(16), vp(16), vp(16), ctypes.byref(dec),
+                                           ctypes.c_float(0.1), vp(16), None, ctypes.byref(opt),
+                                           None)
+    assert call(csa.make_attn_options(-1, 256)) == E
+    assert call(csa.make_attn_options(1, -3)) == E
+    o = csa.make_attn_options(4, 256)
+    o.reserved = 1
+    assert call(o) == E
+    # a caller workspace smaller than the plan, or misaligned
+    need = attn_plan(dec, entry_splits=4)[1]
+    assert call(csa.make_attn_options(4, 256, 256, need - 1)) == B.CSA_ERR_WORKSPACE
+    assert call(csa.make_attn_options(4, 256, 256 + 64, need)) == B.CSA_ERR_WORKSPACE
+    assert lib.csa_sparse_attention_workspace_bytes(None, None, None) == 0

@@ -181,3 +181,72 @@ def test_composite_after_indexer(csa):
     compare_exact(out_idx[0].cpu().numpy(), out_score[0].cpu().numpy(), o_idx, o_score, rows)
     att["idx"] = torch.from_numpy(o_idx[None]).cuda()   # the oracle's lists
     _check_rows(att, aw, out, lse, {0: rows})
+
+
+# ---------------------------------------------------------------- entry ranges
+
+def _splits(csa, aw, G):
+    return csa.attention_plan(csa.make_attn_desc(aw.B, aw.S, aw.T, aw.H, aw.D, aw.n_sel),
+                              csa.make_attn_options(G))[0]
+
+
+@pytest.mark.parametrize("G", [0, 2, 5, 64])
+def test_entry_splits_decode(csa, G):
+    """64 rows at the end of a 262,144-position context: each row's 2,048
+    entries split into ranges (automatic, or 2, 5, 64 of them); every row
+    against the oracle."""
+    aw = ATTN_WORKLOADS["attn-dec64"]
+    got = _splits(csa, aw, G)
+    print(f"\n[case] {aw} entry_splits={G} -> {got}", flush=True)
+    assert got > 1
+    inp = make_attn_inputs(aw, seed=7, device="cuda")
+    out, lse = csa.sparse_attention(inp["q"], inp["k"], inp["v"], inp["idx"], entry_splits=G)
+    torch.cuda.synchronize()
+    stats = _check_rows(inp, aw, out, lse, _all_rows(aw))
+    print(f"[attn] {stats}", flush=True)
+
+
+@pytest.mark.parametrize("H,D", [(32, 64), (64, 128), (128, 64), (128, 128)])
+def test_entry_splits_short_lists(csa, H, D):
+    """Rows whose lists are shorter than one range (empty ranges, rows with
+    no entry at all) and rows whose lists fill several ranges."""
+    for off in (0, 1000):
+        aw = AttnWorkload(f"split{off}", B=2, S=40, T=3000, H=H, D=D, n_sel=600, row_offset=off)
+        print(f"\n[case] {aw} entry_splits=4", flush=True)
+        inp = make_attn_inputs(aw, seed=8, device="cuda")
+        out, lse = csa.sparse_attention(inp["q"], inp["k"], inp["v"], inp["idx"], entry_splits=4)
+        torch.cuda.synchronize()
+        _check_rows(inp, aw, out, lse, _all_rows(aw))
+
+
+def test_entry_splits_padding_anywhere(csa):
+    aw = AttnWorkload("mixed-split", B=1, S=50, T=900, H=64, D=128, n_sel=700, m=1)
+    inp = make_attn_inputs(aw, seed=9, device="cuda")
+    idx = inp["idx"].cpu().numpy()
+    rng = np.random.default_rng(9)
+    for t in range(aw.S):
+        row = idx[0, t]
+        holes = rng.random(aw.n_sel) < 0.4
+        row[holes] = rng.choice([-1, -3, aw.T, aw.T + 9], size=holes.sum())
+        if t % 5 == 0:
+            row[200:500] = -1              # whole ranges without a valid entry
+        rng.shuffle(row)
+    inp["idx"] = torch.from_numpy(idx).cuda()
+    print(f"\n[case] {aw} entry_splits=3", flush=True)
+    out, lse = csa.sparse_attention(inp["q"], inp["k"], inp["v"], inp["idx"], entry_splits=3)
+    torch.cuda.synchronize()
+    _check_rows(inp, aw, out, lse, _all_rows(aw))
+
+
+def test_entry_splits_caller_workspace(csa):
+    """A caller workspace with stale content gives the same bits as the
+    library-allocated one; repeated calls are bit-identical."""
+    aw = ATTN_WORKLOADS["attn-dec64"]
+    inp = make_attn_inputs(aw, seed=10, device="cuda")
+    a_out, a_lse = csa.sparse_attention(inp["q"], inp["k"], inp["v"], inp["idx"], entry_splits=0)
+    ws = csa.attention_workspace_for(inp["q"], inp["k"], aw.n_sel, entry_splits=0)
+    ws.fill_(0x7F)
+    b_out, b_lse = csa.sparse_attention(inp["q"], inp["k"], inp["v"], inp["idx"], entry_splits=0,
+                                        workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a_out, b_out) and torch.equal(a_lse, b_lse)
