@@ -116,9 +116,9 @@ __device__ __forceinline__ void bitonic_step(unsigned long long (&key)[E], int l
                 lane_xor<D>(uint32_t(key[e]), lane);
             const bool up = ((lane * E + e) & SIZE) == 0;
             const bool keep_min = lower == up;
-            const unsigned long long mn = key[e] < o ? key[e] : o;
-            const unsigned long long mx = key[e] < o ? o : key[e];
-            key[e] = keep_min ? mn : mx;
+            // the partner's key replaces ours when it is the one to keep
+            const bool take = (key[e] < o) != keep_min;
+            key[e] = take ? o : key[e];
         }
     }
     if constexpr (STRIDE > 1) bitonic_step<E, SIZE, STRIDE / 2>(key, lane);

@@ -95,3 +95,52 @@ def test_concurrent_streams(csa, inputs):
     torch.cuda.synchronize()
     for oi, os_ in outs:
         assert torch.equal(oi, ref_idx) and torch.equal(os_, ref_score)
+
+
+def test_attention_graph_capture_and_streams(csa):
+    """csa_sparse_attention allocates nothing, and with a caller workspace
+    the range-split form only enqueues kernels too: both can be captured
+    into a HIP graph, and every replay (with eager work between) matches
+    the eager call.  Two streams running split calls with their own
+    workspaces at the same time also match."""
+    from csa_synth import ATTN_WORKLOADS, make_attn_inputs
+    aw = ATTN_WORKLOADS["attn-dec64"]
+    inp = make_attn_inputs(aw, seed=12, device="cuda")
+    args = (inp["q"], inp["k"], inp["v"], inp["idx"])
+    for G in (1, 0):
+        ref_out, ref_lse = csa.sparse_attention(*args, entry_splits=G)
+        torch.cuda.synchronize()
+        ws = csa.attention_workspace_for(inp["q"], inp["k"], aw.n_sel, entry_splits=G)
+        out = torch.empty_like(ref_out)
+        lse = torch.empty_like(ref_lse)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                csa.sparse_attention(*args, out=out, lse=lse, entry_splits=G, workspace=ws,
+                                     stream=side)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            out.fill_(3)
+            lse.fill_(3.0)
+            ws.fill_(rep + 1)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), f"G={G} replay {rep}"
+            csa.sparse_attention(*args, entry_splits=G)  # eager work between the replays
+
+    ref_out, ref_lse = csa.sparse_attention(*args, entry_splits=0)
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    wss = [csa.attention_workspace_for(inp["q"], inp["k"], aw.n_sel, 0) for _ in streams]
+    outs = [(torch.empty_like(ref_out), torch.empty_like(ref_lse)) for _ in streams]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        for st, ws, (o, l) in zip(streams, wss, outs):
+            with torch.cuda.stream(st):
+                csa.sparse_attention(*args, out=o, lse=l, entry_splits=0, workspace=ws, stream=st)
+    torch.cuda.synchronize()
+    for o, l in outs:
+        assert torch.equal(o, ref_out) and torch.equal(l, ref_lse)
