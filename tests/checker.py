@@ -2,7 +2,7 @@
 
 Acceptance, per the indexer's definition (StreamIndex: Memory-Bounded
 Compressed Sparse Attention via Streaming Top-k, Abstract: the k best keys
-of each query, judged by how much of the exact top-k set is recovered):
+of each query, measured by how much of the exact top-k set is recovered):
 
 * exact inputs (integer-valued, every fp32 partial sum exact): indices and
   scores identical to the oracle, element by element;

@@ -282,3 +282,38 @@ def test_sparse_attention_ex_validation(lib):
     assert call(csa.make_attn_options(4, 256, 256, need - 1)) == B.CSA_ERR_WORKSPACE
     assert call(csa.make_attn_options(4, 256, 256 + 64, need)) == B.CSA_ERR_WORKSPACE
     assert lib.csa_sparse_attention_workspace_bytes(None, None, None) == 0
+
+
+def test_header_is_plain_c(tmp_path):
+    """include/csa_index.h compiles as C99 and C++17 on its own (with only
+    the HIP runtime API header) and every declared entry point is callable
+    with the documented argument types."""
+    import shutil
+    import subprocess
+    rocm_inc = "/opt/rocm/include"
+    if not os.path.isdir(rocm_inc) or shutil.which("gcc") is None:
+        pytest.skip("no ROCm headers or gcc")
+    src = tmp_path / "use.c"
+    src.write_text('''#include "csa_index.h"
+int use(void) {
+    csa_desc d = {1, 16, 4, 64, 128, CSA_BF16, 0, 0, 0};
+    csa_options o = {0};
+    csa_plan_info info;
+    csa_attn_desc ad = {1, 16, 4, 64, 128, 8, 0};
+    csa_attn_options ao = {0};
+    int32_t g = 0;
+    size_t n = csa_workspace_bytes(&d, 4, 8, &o) + csa_sparse_attention_workspace_bytes(&ad, &ao, &g);
+    int rc = csa_plan_query(&d, 4, 8, &o, &info);
+    rc |= csa_index(0, 0, 0, &d, 4, 8, 0, 0, 0) | csa_index_ex(0, 0, 0, &d, 4, 8, 0, 0, &o, 0);
+    rc |= csa_sparse_attention(0, 0, 0, 0, &ad, 0.1f, 0, 0, 0);
+    rc |= csa_sparse_attention_ex(0, 0, 0, 0, &ad, 0.1f, 0, 0, &ao, 0);
+    return rc + (int)n + (csa_status_string(rc) != 0);
+}
+''')
+    for compiler, std in (("gcc", "-std=c99"), ("g++", "-std=c++17")):
+        cmd = [compiler, std, "-x", "c" if compiler == "gcc" else "c++", "-fsyntax-only",
+               "-Wall", "-Wextra", "-Werror", "-Wno-missing-field-initializers",
+               "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+               "-I", rocm_inc, str(src)]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        assert res.returncode == 0, res.stderr[-2000:]
