@@ -16,8 +16,10 @@ namespace csa {
 
 // Sorts each row of k (index, score) pairs by (score desc, index asc);
 // padding (-1, -inf) sorts last.  pow2 = next power of two >= k entries of
-// 64-bit keys live in dynamic LDS.
-__global__ void __launch_bounds__(256)
+// 64-bit keys live in dynamic LDS; NT threads share a row (256 for rows wider
+// than a wave sorts, 1,024 when there are fewer rows than compute units).
+template <int NT>
+__global__ void __launch_bounds__(NT)
 sort_rows_kernel(int32_t *out_idx, float *out_score, int64_t nrows, int k, int pow2)
 {
     extern __shared__ unsigned long long s_key[];
@@ -25,7 +27,7 @@ sort_rows_kernel(int32_t *out_idx, float *out_score, int64_t nrows, int k, int p
     for (int64_t row = blockIdx.x; row < nrows; row += gridDim.x) {
         int32_t *ri = out_idx + row * k;
         float *rs = out_score + row * k;
-        for (int e = tid; e < pow2; e += 256) {
+        for (int e = tid; e < pow2; e += NT) {
             unsigned long long key = ~0ull;
             if (e < k) {
                 const uint32_t u = order_key(rs[e]);
@@ -36,8 +38,8 @@ sort_rows_kernel(int32_t *out_idx, float *out_score, int64_t nrows, int k, int p
         __syncthreads();
         for (int size = 2; size <= pow2; size <<= 1) {
             for (int stride = size >> 1; stride > 0; stride >>= 1) {
-                for (int i = tid; i < pow2 / 2; i += 256) {
-                    const int lo = 2 * stride * (i / stride) + (i % stride);
+                for (int i = tid; i < pow2 / 2; i += NT) {
+                    const int lo = ((i & ~(stride - 1)) << 1) | (i & (stride - 1));
                     const int hi = lo + stride;
                     const bool up = (lo & size) == 0;
                     const unsigned long long x = s_key[lo], y = s_key[hi];
@@ -49,7 +51,7 @@ sort_rows_kernel(int32_t *out_idx, float *out_score, int64_t nrows, int k, int p
                 __syncthreads();
             }
         }
-        for (int e = tid; e < k; e += 256) {
+        for (int e = tid; e < k; e += NT) {
             const unsigned long long key = s_key[e];
             ri[e] = int32_t(uint32_t(key));
             rs[e] = key_to_float(~uint32_t(key >> 32));
@@ -219,7 +221,10 @@ hipError_t launch_sort_rows(const Plan &p, int32_t *out_idx, float *out_score, i
 {
     const int64_t nrows = p.B * p.S;
     if (nrows == 0) return hipSuccess;
-    switch (p.sort_pow2 <= 64 ? 64 : p.sort_pow2) {
+    // fewer rows than compute units: one wave per row would leave each row's
+    // long serial network alone on its CU; a workgroup per row is quicker
+    const bool few = nrows < num_cus && p.sort_pow2 >= 256;
+    switch (few ? 0 : p.sort_pow2 <= 64 ? 64 : p.sort_pow2) {
     case 64: return launch_sort_wave<1>(nrows, p.k, num_cus, out_idx, out_score, s);
     case 128: return launch_sort_wave<2>(nrows, p.k, num_cus, out_idx, out_score, s);
     case 256: return launch_sort_wave<4>(nrows, p.k, num_cus, out_idx, out_score, s);
@@ -231,13 +236,24 @@ hipError_t launch_sort_rows(const Plan &p, int32_t *out_idx, float *out_score, i
     const int64_t want = int64_t(num_cus) * 8;
     const int grid = int(nrows < want ? nrows : want);
     const size_t lds = size_t(p.sort_pow2) * sizeof(unsigned long long);
+    if (few) {
+        if (lds > 65536) {
+            const hipError_t e = hipFuncSetAttribute(
+                reinterpret_cast<const void *>(sort_rows_kernel<1024>),
+                hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+            if (e != hipSuccess) return e;
+        }
+        hipLaunchKernelGGL(sort_rows_kernel<1024>, dim3(grid), dim3(1024), lds, s, out_idx,
+                           out_score, nrows, p.k, p.sort_pow2);
+        return hipGetLastError();
+    }
     if (lds > 65536) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(sort_rows_kernel),
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(sort_rows_kernel<256>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
                                                  int(lds));
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(sort_rows_kernel, dim3(grid), dim3(256), lds, s, out_idx, out_score,
+    hipLaunchKernelGGL(sort_rows_kernel<256>, dim3(grid), dim3(256), lds, s, out_idx, out_score,
                        nrows, p.k, p.sort_pow2);
     return hipGetLastError();
 }
