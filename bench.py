@@ -151,7 +151,7 @@ def attention(csa, args):
     att = make_attn_inputs(aw, seed=0, device=dev)
     cpu = None
     if not args.no_cpu_baseline and not args.composite:
-        cpu = attn_cpu_baseline(att, aw, args.cpu_rows // 4)
+        cpu = attn_cpu_baseline(att, aw, 2 * args.cpu_rows)
     ind = None
     if args.composite:
         wl = WORKLOADS[INDEXER_FOR[aw.name]]
