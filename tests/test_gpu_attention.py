@@ -250,3 +250,32 @@ def test_entry_splits_caller_workspace(csa):
                                         workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(a_out, b_out) and torch.equal(a_lse, b_lse)
+
+
+@pytest.mark.parametrize("G", [1, 3])
+def test_equal_weights_exact_mean(csa, G):
+    """scale = 0 makes every weight exactly 1 (bf16 of 2^0): with integer
+    values the weighted sum and the weight count are exact in fp32, so the
+    output is bf16(f32(sum v) * f32(1 / n)), bit for bit, with and without
+    entry ranges; lse = log(n)."""
+    aw = AttnWorkload("mean", B=2, S=96, T=300, H=64, D=128, n_sel=200, m=1)
+    inp = make_attn_inputs(aw, seed=13, device="cuda")
+    g = torch.Generator(device="cpu").manual_seed(13)
+    v = torch.randint(-3, 4, (aw.B, aw.T, aw.D), generator=g).to(torch.bfloat16).cuda()
+    out, lse = csa.sparse_attention(inp["q"], inp["k"], v, inp["idx"], 0.0, entry_splits=G)
+    torch.cuda.synchronize()
+    idx = inp["idx"].cpu().numpy()
+    vf = v.float().cpu().numpy()
+    got = out.float().cpu().numpy()
+    got_lse = lse.cpu().numpy()
+    for b in range(aw.B):
+        for t in range(aw.S):
+            sel = idx[b, t][(idx[b, t] >= 0) & (idx[b, t] < aw.T)]
+            n = len(sel)
+            if n == 0:
+                assert np.all(got[b, t] == 0) and np.all(np.isneginf(got_lse[b, t]))
+                continue
+            s = vf[b, sel].sum(axis=0).astype(np.float32)          # exact: small integers
+            want = torch.from_numpy(s * (np.float32(1) / np.float32(n))).to(torch.bfloat16)
+            assert np.array_equal(got[b, t], np.broadcast_to(want.float().numpy(), (aw.H, aw.D))), (b, t)
+            np.testing.assert_allclose(got_lse[b, t], np.log(n), rtol=1e-6)
