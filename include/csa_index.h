@@ -202,7 +202,7 @@ const char *csa_status_string(int status);
  *   out  [B, S, H, D]   bf16   (device)
  *   lse  [B, S, H]      fp32   (device; may be NULL)
  * Supported: H in {32, 64, 128}, D in {64, 128}; B >= 1, S >= 0, T >= 0,
- * n_sel >= 0.  Other H or D return CSA_ERR_UNSUPPORTED.  q, k, v and out
+ * 0 <= n_sel <= 2^31 - 65.  Other H or D return CSA_ERR_UNSUPPORTED.  q, k, v and out
  * must be 16-byte aligned, idx and lse 4-byte aligned.
  */
 typedef struct {

@@ -183,6 +183,8 @@ int attn_plan(const csa_attn_desc *desc, const csa_attn_options *opt, AttnPlan *
     const csa_attn_desc &d = *desc;
     if (d.B < 1 || d.S < 0 || d.T < 0 || d.n_sel < 0 || d.reserved0 != 0)
         return CSA_ERR_INVALID_ARG;
+    // list positions (entry + tile padding) are 32-bit in the kernel
+    if (d.n_sel > INT32_MAX - 64) return CSA_ERR_INVALID_ARG;
     if (!((d.H == 32 || d.H == 64 || d.H == 128) && (d.D == 64 || d.D == 128)))
         return CSA_ERR_UNSUPPORTED;
     // element counts must stay addressable with 64-bit byte offsets

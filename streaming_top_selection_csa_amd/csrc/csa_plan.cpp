@@ -52,9 +52,10 @@ int make_plan(const csa_desc *desc, int32_t m, int32_t k,
     // positions must stay representable: t + 1 fits comfortably in int64
     if (desc->S > (int64_t(1) << 40) || row_offset > (int64_t(1) << 40))
         return CSA_ERR_INVALID_ARG;
-    // element counts must fit the 64-bit offsets used by the kernels
+    // element counts must fit the 64-bit offsets used by the kernels (checked
+    // before multiplying: a signed overflow would already be undefined)
+    if (desc->S > 0 && desc->B > INT64_MAX / desc->S) return CSA_ERR_INVALID_ARG;
     const int64_t rows = desc->B * desc->S;
-    if (desc->S > 0 && rows / desc->S != desc->B) return CSA_ERR_INVALID_ARG;
     if (rows > (int64_t(1) << 46) / (int64_t(desc->H) * desc->D)) return CSA_ERR_INVALID_ARG;
     if (rows > (int64_t(1) << 46) / k) return CSA_ERR_INVALID_ARG;
 

@@ -328,3 +328,29 @@ def test_bench_refuses_more_than_one_gpu():
                          capture_output=True, text=True, timeout=120)
     assert res.returncode == 2
     assert "one GPU" in res.stderr and res.stdout == ""
+
+
+def test_host_code_fuzz_under_sanitizers(tmp_path):
+    """The planning and validation code of the C ABI, built for the host
+    with AddressSanitizer and UBSan (no device code: the HIP runtime and
+    the kernel launchers are stubbed), survives 200,000 random, extreme and
+    hostile argument sets with consistent plans."""
+    import shutil
+    import subprocess
+    rocm_inc = "/opt/rocm/include"
+    if not os.path.isdir(rocm_inc) or shutil.which("g++") is None:
+        pytest.skip("no ROCm headers or g++")
+    csrc = os.path.join(ROOT, "streaming_top_selection_csa_amd", "csrc")
+    exe = tmp_path / "fuzz_abi_host"
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", "-D__HIP_PLATFORM_AMD__", "-I", rocm_inc,
+           "-I", os.path.join(ROOT, "include"), "-I", csrc,
+           os.path.join(ROOT, "tests", "fuzz_abi_host.cpp"), os.path.join(csrc, "csa_plan.cpp"),
+           os.path.join(csrc, "csa_abi.cpp"), "-o", str(exe)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-3000:]
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0", UBSAN_OPTIONS="print_stacktrace=1")
+    res = subprocess.run([str(exe), "200000"], capture_output=True, text=True, timeout=300,
+                         env=env)
+    assert res.returncode == 0, (res.stdout + res.stderr)[-3000:]
+    assert "fuzz ok" in res.stdout
