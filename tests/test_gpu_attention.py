@@ -149,16 +149,17 @@ def test_deterministic_and_lse_optional(csa):
 
 def test_full_size_sampled_rows(csa):
     """The S=262,144 shape (T=65,536, H=64, D=128, 2,048 entries per row),
-    in the launch configuration the benchmark times; 48 sampled rows per
-    check, including the first rows (short lists) and the last."""
+    in the launch configuration the benchmark times; 256 sampled rows,
+    including the first rows (short and empty lists), the rows where the
+    list first fills (n_vis = 2,048 at position 8,191) and the last."""
     aw = ATTN_WORKLOADS["attn-s256k"]
     print(f"\n[case] {aw}", flush=True)
     inp = make_attn_inputs(aw, seed=0, device="cuda")
     out, lse = csa.sparse_attention(inp["q"], inp["k"], inp["v"], inp["idx"])
     torch.cuda.synchronize()
     rng = np.random.default_rng(0)
-    rows = np.unique(np.r_[[0, 1, 2, 3, 4, 7, 8191, 8192, aw.S - 1],
-                           rng.choice(aw.S, size=39, replace=False)])
+    edges = [0, 1, 2, 3, 4, 7, 8190, 8191, 8192, aw.S - 2, aw.S - 1]
+    rows = np.unique(np.r_[edges, rng.choice(aw.S, size=256 - len(edges), replace=False)])
     stats = _check_rows(inp, aw, out, lse, {0: rows})
     print(f"[attn] {stats}", flush=True)
 
