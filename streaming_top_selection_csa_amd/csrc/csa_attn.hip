@@ -14,7 +14,7 @@
 // from global memory straight into LDS (global_load_lds, 16 bytes per lane)
 // into a ring of two buffers, one tile ahead; at 32 KB of LDS the register
 // budget (two waves per SIMD) is what bounds residency, four workgroups per
-// CU (more resident waves beat deeper rings here).  Each row's 16-byte
+// CU (more resident workgroups beat deeper rings here).  Each row's 16-byte
 // chunks are XOR-swizzled by row, so the operand reads below hit distinct
 // LDS banks.  For every tile each wave
 //   * computes the 32x32 block S^T = K_tile . Q^T of (key, head) scores with
@@ -29,7 +29,7 @@
 //     rows with gfx950's LDS transpose load (ds_read_b64_tr_b16), which
 //     hands each lane one value column at the keys its weights belong to.
 // Rows are mapped to workgroups so that consecutive rows share an XCD (and
-// its L2): queries close in position tend to pick the same keys.
+// its L2), where queries close in position may pick the same keys.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -80,7 +80,6 @@ __device__ __forceinline__ float pair_sum(float x)
 // s_waitcnt immediate: at most n vector-memory loads of this wave in flight,
 // no LDS / scalar access outstanding (lgkmcnt 0), export count untouched.
 constexpr int vm_wait_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4); }
-
 
 // One unit is a query row (SPLIT = false) or one of the n_splits ranges of
 // split_entries entries of a row's list (SPLIT = true: short query blocks,

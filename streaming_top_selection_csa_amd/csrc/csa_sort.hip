@@ -140,8 +140,11 @@ __device__ __forceinline__ void bitonic_sort(unsigned long long (&key)[E], int l
 // stores then cover whole cache lines (consecutive lanes, consecutive
 // elements), and the buffer's one-word pad per 32 keeps each lane's run of
 // E words on distinct banks.
+// Three waves per SIMD: at E = 32 that costs a few spilled registers but
+// beats two waves per SIMD without spills by 12% (the network is latency-
+// bound: 64-bit compares, lane permutes, swizzles); the smaller E fit anyway.
 template <int E>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
 sort_rows_wave_kernel(int32_t *out_idx, float *out_score, int64_t nrows, int k)
 {
     constexpr int N = 64 * E;
