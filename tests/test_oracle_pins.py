@@ -328,8 +328,9 @@ def test_k_beyond_keys_and_empty_rows(oracle_lib):
 
 
 def test_materialized_tensor_closed_form():
-    """The dense [B,S,H_I,T] fp32 score tensor at S=65,536, H_I=64, m=4 is
-    2**38 bytes = 256 GiB, the figure the abstract gives for it."""
+    """Materialising every per-head score as fp32, [B,S,H_I,T] at S=65,536,
+    H_I=64, m=4, takes 2**38 bytes = 256 GiB, the figure the abstract gives
+    for it."""
     from csa_synth import WORKLOADS
     wl = WORKLOADS["s64k"]
     assert wl.B * wl.S * wl.H * wl.n_keys * 4 == 256 * 2 ** 30
