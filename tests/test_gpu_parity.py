@@ -108,3 +108,28 @@ def test_s16k_sample(csa):
     rows = sample_rows(wl.S, wl.m, wl.k, n=512)
     _, _, stats = _check(csa, wl, rows=rows)
     print(stats)
+
+
+def test_max_k_many_rows(csa):
+    """k = 16,384 (the largest supported): rows sorted by the 256-thread LDS
+    sort in 128 KB of LDS; sampled rows around n_vis = k, exact."""
+    wl = Workload("maxk", B=1, S=20000, m=1, H=4, D=32, k=16384, dist="int")
+    rng = np.random.default_rng(16384)
+    rows = np.unique(np.r_[[0, 1, 100, 16382, 16383, 16384, 16385, 19998, 19999],
+                           rng.choice(20000, size=40, replace=False)])
+    _check(csa, wl, seed=3, rows=rows)
+
+
+def test_max_k_few_rows(csa):
+    """k = 16,384 with fewer rows than compute units: the 1,024-thread LDS
+    sort; every row sees about 19,000 keys; all rows exact."""
+    wl = Workload("maxk-few", B=1, S=40, m=1, H=4, D=32, k=16384, dist="int", T=20000,
+                  row_offset=19000)
+    print(f"\n[case] {wl}", flush=True)
+    inp = make_inputs(wl, seed=4, device="cuda")
+    out_idx, out_score = _run(csa, inp, wl, row_offset=wl.row_offset)
+    view = OracleView(inp, wl, 0)
+    rows = np.arange(wl.S, dtype=np.int64)
+    o_idx, o_score = view.topk(rows, rows + wl.row_offset, wl.k, wl.m)
+    compare_exact(out_idx[0].cpu().numpy(), out_score[0].cpu().numpy(), o_idx, o_score,
+                  rows + wl.row_offset)
