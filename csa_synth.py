@@ -236,6 +236,8 @@ ATTN_WORKLOADS = {
     # the indexer's S = 262,144 shape: the composite step at that length
     "attn-s256k": AttnWorkload("attn-s256k", B=1, S=262144, T=65536, H=64, D=128, n_sel=2048),
     "attn-s64k": AttnWorkload("attn-s64k", B=1, S=65536, T=16384, H=64, D=128, n_sel=2048),
+    # the indexer's largest shape, S = 1,048,576
+    "attn-s1m": AttnWorkload("attn-s1m", B=1, S=1048576, T=262144, H=64, D=128, n_sel=2048),
     "attn-small": AttnWorkload("attn-small", B=2, S=700, T=175, H=64, D=128, n_sel=100),
     # 64 positions at the end of a 262,144-position context (a decode step)
     "attn-dec64": AttnWorkload("attn-dec64", B=1, S=64, T=65536, H=64, D=128, n_sel=2048,

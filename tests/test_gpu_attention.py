@@ -164,6 +164,21 @@ def test_full_size_sampled_rows(csa):
     print(f"[attn] {stats}", flush=True)
 
 
+def test_s1m_sampled_rows(csa):
+    """The largest shape, S=1,048,576 and T=262,144 (43 GB of q, lists and
+    output): 128 sampled rows against the oracle."""
+    aw = ATTN_WORKLOADS["attn-s1m"]
+    print(f"\n[case] {aw}", flush=True)
+    inp = make_attn_inputs(aw, seed=0, device="cuda")
+    out, lse = csa.sparse_attention(inp["q"], inp["k"], inp["v"], inp["idx"])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    edges = [0, 5, 8191, 8192, aw.S - 1]
+    rows = np.unique(np.r_[edges, rng.choice(aw.S, size=128 - len(edges), replace=False)])
+    stats = _check_rows(inp, aw, out, lse, {0: rows})
+    print(f"[attn] {stats}", flush=True)
+
+
 def test_composite_after_indexer(csa):
     """The indexer's top-k list feeds the attention: on integer indexer
     inputs the lists equal the oracle's bit for bit, so the attention of
