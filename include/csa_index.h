@@ -69,8 +69,8 @@ typedef enum {
  *   q_scale [B, S, H]     fp32 > 0   (device; fp8 only, NULL for bf16)
  *   k_scale [B, T]        fp32 > 0   (device; fp8 only, NULL for bf16)
  * Supported: H in {1, 2, 4, 8, 16, 32, 64}; D in {32, 64, 128} for bf16 and
- * {64, 128} for fp8; B >= 1, S >= 0, T >= 0.  Other combinations return
- * CSA_ERR_UNSUPPORTED.
+ * {64, 128} for fp8; B >= 1, S >= 0, 0 <= T <= 2^30.  Other (dtype, H, D)
+ * combinations return CSA_ERR_UNSUPPORTED, other sizes CSA_ERR_INVALID_ARG.
  */
 typedef struct {
     int64_t B;
@@ -110,7 +110,10 @@ typedef struct {
  *                per 64 visible keys).  The partial lists take B*S*G*k*8
  *                bytes of workspace, capped at 1 GiB by lowering G.  Affects
  *                speed and workspace only, never the result.
- *   reserved1    Must be 0.
+ *   flags        0, or CSA_FLAG_NO_SCORE: the call will pass out_score = NULL.
+ *                Only csa_workspace_bytes and csa_plan_query read it (a call
+ *                with out_score = NULL plans for that by itself); other bits
+ *                must be 0.
  */
 typedef struct {
     int32_t chunk_keys;
@@ -120,8 +123,11 @@ typedef struct {
     size_t workspace_bytes;
     hipEvent_t timing[2];
     int32_t key_splits;
-    int32_t reserved1;
+    int32_t flags;
 } csa_options;
+
+/* csa_options.flags: size the workspace for calls without a score output. */
+#define CSA_FLAG_NO_SCORE 1
 
 /* What a call will do; filled by csa_plan_query (host only, no device work). */
 typedef struct {
@@ -138,9 +144,14 @@ typedef struct {
 /*
  * csa_index: top-k compressed keys for every query position.
  *   out_idx   [B, S, k] int32 (device): key indices, -1 = padding.
- *   out_score [B, S, k] fp32  (device): scores, -inf = padding.
- * Both outputs are required.  Uses default options (library-allocated
- * workspace).  Returns CSA_OK or a negative csa_status.
+ *   out_score [B, S, k] fp32  (device): scores, -inf = padding; NULL = the
+ *             scores are not returned.  out_idx is identical either way.
+ *             Rows of next_pow2(k) <= 2048 keys without key ranges are
+ *             sorted inside the scoring kernel and need no score storage at
+ *             all; otherwise a separate sort pass keeps the scores in the
+ *             workspace (B*S*k*4 more bytes, see csa_workspace_bytes).
+ * Uses default options (library-allocated workspace).  Returns CSA_OK or a
+ * negative csa_status.
  */
 int csa_index(const void *q, const float *w, const void *k_cmp,
               const csa_desc *desc, int32_t m, int32_t k,
@@ -156,7 +167,10 @@ int csa_index_ex(const void *q, const float *w, const void *k_cmp,
  * arguments).  With one key range (key_splits resolving to 1, always the
  * case when the query blocks fill the device) it is independent of S and T
  * and scales with the number of resident queries and k + chunk_keys only;
- * G > 1 key ranges add B*S*G*k*8 bytes for the partial lists. */
+ * G > 1 key ranges add B*S*G*k*8 bytes for the partial lists.  With
+ * CSA_FLAG_NO_SCORE in opt->flags it is the size for out_score = NULL,
+ * which adds B*S*k*4 bytes only when the rows are sorted by a separate pass
+ * (key ranges, or next_pow2(k) > 2048). */
 size_t csa_workspace_bytes(const csa_desc *desc, int32_t m, int32_t k,
                            const csa_options *opt);
 

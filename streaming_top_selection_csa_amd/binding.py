@@ -27,6 +27,8 @@ CSA_ERR_HIP = -4
 CSA_BF16 = 0
 CSA_FP8_E4M3FN = 1
 
+CSA_FLAG_NO_SCORE = 1
+
 EXPORTS = ("csa_index", "csa_index_ex", "csa_workspace_bytes", "csa_plan_query",
            "csa_status_string", "csa_sparse_attention", "csa_sparse_attention_ex",
            "csa_sparse_attention_workspace_bytes")
@@ -43,7 +45,7 @@ class CsaOptions(ctypes.Structure):
     _fields_ = [("chunk_keys", ctypes.c_int32), ("num_cus", ctypes.c_int32),
                 ("row_offset", ctypes.c_int64), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t), ("timing", ctypes.c_void_p * 2),
-                ("key_splits", ctypes.c_int32), ("reserved1", ctypes.c_int32)]
+                ("key_splits", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
 
 class CsaPlanInfo(ctypes.Structure):
@@ -121,9 +123,10 @@ def make_desc(B, S, T, H, D, dtype=CSA_BF16, q_scale_ptr=0, k_scale_ptr=0) -> Cs
 
 
 def make_options(chunk_keys=0, row_offset=0, num_cus=0, workspace=None, workspace_bytes=0,
-                 timing=(None, None), key_splits=0) -> CsaOptions:
+                 timing=(None, None), key_splits=0, flags=0) -> CsaOptions:
     opt = CsaOptions()
     opt.key_splits = int(key_splits)
+    opt.flags = int(flags)
     opt.chunk_keys = int(chunk_keys)
     opt.num_cus = int(num_cus)
     opt.row_offset = int(row_offset)
@@ -171,14 +174,16 @@ def index(q: torch.Tensor, w: torch.Tensor, k_cmp: torch.Tensor, m: int, k: int,
           out_idx: Optional[torch.Tensor] = None, out_score: Optional[torch.Tensor] = None,
           chunk_keys: int = 0, row_offset: int = 0, key_splits: int = 0,
           workspace: Optional[torch.Tensor] = None, timing=None,
-          stream: Optional[torch.cuda.Stream] = None):
+          stream: Optional[torch.cuda.Stream] = None, want_score: bool = True):
     """Top-k compressed keys per query position (csa_index_ex).
 
     q [B,S,H,D] bf16 | e4m3fn, w [B,S,H] fp32, k_cmp [B,T,D] same dtype as
     q; for fp8 also q_scale [B,S,H] and k_scale [B,T] fp32.  Returns
-    (out_idx int32 [B,S,k], out_score fp32 [B,S,k]).  `timing` is an
-    optional pair of raw hipEvent_t handles recorded around the scoring
-    kernel.  Asynchronous on `stream` (default: torch's current stream).
+    (out_idx int32 [B,S,k], out_score fp32 [B,S,k]); with want_score=False
+    no score output is passed (out_score = NULL) and the second item is
+    None.  `timing` is an optional pair of raw hipEvent_t handles recorded
+    around the scoring kernel.  Asynchronous on `stream` (default: torch's
+    current stream).
     """
     lib = load_library()
     dt = _dtype_code(q)
@@ -204,12 +209,18 @@ def index(q: torch.Tensor, w: torch.Tensor, k_cmp: torch.Tensor, m: int, k: int,
         raise ValueError("scales are only used with fp8 inputs")
     if out_idx is None:
         out_idx = torch.empty((B, S, k), dtype=torch.int32, device=q.device)
-    if out_score is None:
+    if not want_score:
+        if out_score is not None:
+            raise ValueError("out_score given with want_score=False")
+    elif out_score is None:
         out_score = torch.empty((B, S, k), dtype=torch.float32, device=q.device)
     _check(out_idx, "out_idx", torch.int32)
-    _check(out_score, "out_score", torch.float32)
-    if tuple(out_idx.shape) != (B, S, k) or tuple(out_score.shape) != (B, S, k):
+    if tuple(out_idx.shape) != (B, S, k):
         raise ValueError("outputs must be [B,S,k]")
+    if out_score is not None:
+        _check(out_score, "out_score", torch.float32)
+        if tuple(out_score.shape) != (B, S, k):
+            raise ValueError("outputs must be [B,S,k]")
     desc = make_desc(B, S, T, H, D, dt, qs_ptr, ks_ptr)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
@@ -220,7 +231,8 @@ def index(q: torch.Tensor, w: torch.Tensor, k_cmp: torch.Tensor, m: int, k: int,
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     rc = lib.csa_index_ex(q.data_ptr(), w.data_ptr(), k_cmp.data_ptr(), ctypes.byref(desc),
-                          int(m), int(k), out_idx.data_ptr(), out_score.data_ptr(),
+                          int(m), int(k), out_idx.data_ptr(),
+                          out_score.data_ptr() if out_score is not None else None,
                           ctypes.byref(opt), ctypes.c_void_p(stream.cuda_stream))
     if rc != CSA_OK:
         raise CsaError(rc, "csa_index_ex")
@@ -310,13 +322,16 @@ def sparse_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: tor
 
 
 def workspace_for(q: torch.Tensor, k_cmp: torch.Tensor, m: int, k: int, chunk_keys: int = 0,
-                  row_offset: int = 0, key_splits: int = 0) -> torch.Tensor:
-    """A torch-allocated workspace big enough for `index` on these inputs."""
+                  row_offset: int = 0, key_splits: int = 0,
+                  want_score: bool = True) -> torch.Tensor:
+    """A torch-allocated workspace big enough for `index` on these inputs
+    (with want_score=False: for calls without a score output)."""
     B, S, H, D = q.shape
     desc = make_desc(B, S, k_cmp.shape[1], H, D, _dtype_code(q),
                      1 if q.dtype == torch.float8_e4m3fn else 0,
                      1 if q.dtype == torch.float8_e4m3fn else 0)
-    n = workspace_bytes(desc, m, k, make_options(chunk_keys, row_offset, key_splits=key_splits))
+    n = workspace_bytes(desc, m, k, make_options(chunk_keys, row_offset, key_splits=key_splits,
+                                                 flags=0 if want_score else CSA_FLAG_NO_SCORE))
     if n == 0:
         raise CsaError(CSA_ERR_INVALID_ARG, "csa_workspace_bytes")
     return torch.empty(n, dtype=torch.uint8, device=q.device)

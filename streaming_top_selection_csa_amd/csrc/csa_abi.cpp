@@ -3,8 +3,9 @@
 // Every call validates and plans on the host first (nothing touches the
 // device on an invalid call), then enqueues, on the caller's stream: the
 // scoring kernel (scores + running top-k per query position, or per key
-// range), the merge of the key ranges' lists when there are several, and
-// the row sort.  No host synchronisation, no host<->device copies.
+// range; rows of up to 2,048 keys leave it sorted), the merge of the key
+// ranges' lists when there are several, and the row sort when the kernel
+// did not sort.  No host synchronisation, no host<->device copies.
 #include <hip/hip_runtime_api.h>
 
 #include <cstdint>
@@ -28,19 +29,19 @@ int device_cus(int *out)
 }
 
 int plan_for(const csa_desc *desc, int32_t m, int32_t k, const csa_options *opt,
-             csa::Plan *p, int *cus)
+             csa::Plan *p, int *cus, bool no_score = false)
 {
     int num_cus = (opt && opt->num_cus > 0) ? opt->num_cus : 0;
     if (opt && opt->num_cus < 0) return CSA_ERR_INVALID_ARG;
     // validate everything that does not need the device before asking it
-    const int pre = csa::make_plan(desc, m, k, opt, num_cus > 0 ? num_cus : 1, p);
+    const int pre = csa::make_plan(desc, m, k, opt, num_cus > 0 ? num_cus : 1, p, no_score);
     if (pre != CSA_OK) return pre;
     if (num_cus == 0) {
         const int rc = device_cus(&num_cus);
         if (rc != CSA_OK) return rc;
     }
     *cus = num_cus;
-    return csa::make_plan(desc, m, k, opt, num_cus, p);
+    return csa::make_plan(desc, m, k, opt, num_cus, p, no_score);
 }
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -94,10 +95,10 @@ extern "C" int csa_index_ex(const void *q, const float *w, const void *k_cmp,
 {
     csa::Plan p;
     int cus = 0;
-    int rc = plan_for(desc, m, k, opt, &p, &cus);
+    int rc = plan_for(desc, m, k, opt, &p, &cus, out_score == nullptr);
     if (rc != CSA_OK) return rc;
     const bool rows = p.B * p.S > 0;
-    if (rows && (!q || !w || !out_idx || !out_score)) return CSA_ERR_INVALID_ARG;
+    if (rows && (!q || !w || !out_idx)) return CSA_ERR_INVALID_ARG;
     if (p.T > 0 && !k_cmp) return CSA_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(k_cmp, 16) || !aligned(w, 4) || !aligned(out_idx, 4) ||
         !aligned(out_score, 4) || !aligned(desc->q_scale, 4) || !aligned(desc->k_scale, 4))
@@ -122,13 +123,19 @@ extern "C" int csa_index_ex(const void *q, const float *w, const void *k_cmp,
     a.q_scale = desc->q_scale;
     a.k_scale = desc->k_scale;
     a.out_idx = out_idx;
-    a.out_score = out_score;
+    // without a score output, a separate row sort keeps the scores in the workspace
+    float *const scores = out_score ? out_score
+        : (p.sort_e == 0 ? reinterpret_cast<float *>(static_cast<unsigned char *>(ws) + p.score_offset)
+                         : nullptr);
+    a.out_score = scores;
     a.ws = static_cast<uint32_t *>(ws);
+    // unsorted lists: the ranges' partial lists, or with one range the output
+    // rows themselves (sorted afterwards by the row sort)
     unsigned char *part = static_cast<unsigned char *>(ws) + p.part_offset;
-    a.part_idx = p.n_splits > 1 ? reinterpret_cast<int32_t *>(part) : nullptr;
+    a.part_idx = p.n_splits > 1 ? reinterpret_cast<int32_t *>(part) : out_idx;
     a.part_score = p.n_splits > 1
         ? reinterpret_cast<float *>(part + size_t(p.B * p.S) * size_t(p.n_splits) * size_t(p.k) * 4u)
-        : nullptr;
+        : scores;
     a.B = p.B;
     a.S = p.S;
     a.T = p.T;
@@ -137,9 +144,10 @@ extern "C" int csa_index_ex(const void *q, const float *w, const void *k_cmp,
     a.topk = p.k;
     a.log_cap = p.log_cap;
     a.n_splits = p.n_splits;
-    a.split_keys = p.split_keys;
+    a.split_keys = p.n_splits > 1 ? p.split_keys : int(csa::kMaxKeys);
     a.blocks_per_batch = p.blocks_per_batch;
     a.n_units = p.n_units;
+    a.sort_e = p.sort_e;
 
     rc = CSA_OK;
     if (opt && opt->timing[0] && hipEventRecord(opt->timing[0], stream) != hipSuccess)
@@ -148,10 +156,11 @@ extern "C" int csa_index_ex(const void *q, const float *w, const void *k_cmp,
     if (rc == CSA_OK && opt && opt->timing[1] && hipEventRecord(opt->timing[1], stream) != hipSuccess)
         rc = CSA_ERR_HIP;
     if (rc == CSA_OK &&
-        csa::launch_merge_splits(p, a.part_idx, a.part_score, out_idx, out_score, cus, stream) !=
+        csa::launch_merge_splits(p, a.part_idx, a.part_score, out_idx, scores, cus, stream) !=
             hipSuccess)
         rc = CSA_ERR_HIP;
-    if (rc == CSA_OK && csa::launch_sort_rows(p, out_idx, out_score, cus, stream) != hipSuccess)
+    if (rc == CSA_OK && p.sort_e == 0 &&
+        csa::launch_sort_rows(p, out_idx, scores, cus, stream) != hipSuccess)
         rc = CSA_ERR_HIP;
     if (owned && hipFreeAsync(ws, stream) != hipSuccess && rc == CSA_OK) rc = CSA_ERR_HIP;
     return rc;

@@ -17,7 +17,7 @@ struct StreamArgs {
     const float *q_scale;       // [B, S, H] (fp8) or null
     const float *k_scale;       // [B, T] (fp8) or null
     int32_t *out_idx;           // [B, S, k]
-    float *out_score;           // [B, S, k]
+    float *out_score;           // [B, S, k]; may be null when the rows are sorted in the kernel
     uint32_t *ws;               // candidate logs: grid * 8 waves * QW * log_cap * 8 bytes
     int32_t *part_idx;          // [B, S, G, k] per-key-range top-k lists (G > 1)
     float *part_score;          // [B, S, G, k]
@@ -25,6 +25,7 @@ struct StreamArgs {
     int m, topk, log_cap;
     int n_splits, split_keys;   // G key ranges of split_keys keys (G = 1: all keys)
     int64_t blocks_per_batch, n_units;
+    int sort_e;                 // > 0: rows sorted in the kernel, sort_e keys per lane
 };
 
 hipError_t launch_stream_topk(const Plan &p, const StreamArgs &a, hipStream_t s);

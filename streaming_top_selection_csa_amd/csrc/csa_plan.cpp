@@ -23,11 +23,13 @@ static int64_t next_pow2(int64_t x)
 }
 
 int make_plan(const csa_desc *desc, int32_t m, int32_t k,
-              const csa_options *opt, int num_cus, Plan *plan)
+              const csa_options *opt, int num_cus, Plan *plan, bool no_score)
 {
     if (!desc || !plan || num_cus <= 0) return CSA_ERR_INVALID_ARG;
     if (desc->B < 1 || desc->S < 0 || desc->T < 0) return CSA_ERR_INVALID_ARG;
-    if (desc->T > INT32_MAX - 1) return CSA_ERR_INVALID_ARG;  // int32 key indices
+    // key indices and the kernels' key arithmetic (tile ends, key ranges) are
+    // 32-bit: T <= 2^30 keeps every such sum below 2^31
+    if (desc->T > kMaxKeys) return CSA_ERR_INVALID_ARG;
     if (desc->reserved0 != 0) return CSA_ERR_INVALID_ARG;
     if (m < 1 || k < 1) return CSA_ERR_INVALID_ARG;
     if (desc->dtype != CSA_BF16 && desc->dtype != CSA_FP8_E4M3FN)
@@ -44,7 +46,9 @@ int make_plan(const csa_desc *desc, int32_t m, int32_t k,
     if (opt) {
         if (opt->row_offset < 0 || opt->chunk_keys < 0 || opt->chunk_keys > kMaxChunk)
             return CSA_ERR_INVALID_ARG;
-        if (opt->key_splits < 0 || opt->reserved1 != 0) return CSA_ERR_INVALID_ARG;
+        if (opt->key_splits < 0 || (opt->flags & ~int32_t(CSA_FLAG_NO_SCORE)) != 0)
+            return CSA_ERR_INVALID_ARG;
+        if (opt->flags & CSA_FLAG_NO_SCORE) no_score = true;
         row_offset = opt->row_offset;
         chunk = opt->chunk_keys;
         splits_req = opt->key_splits;
@@ -79,7 +83,7 @@ int make_plan(const csa_desc *desc, int32_t m, int32_t k,
     p.QB = kWaves * p.QW;
     p.blocks_per_batch = (desc->S + p.QB - 1) / p.QB;
     p.n_blocks = p.blocks_per_batch * desc->B;
-    const int64_t resident = int64_t(num_cus);  // one 8-wave workgroup per CU
+    const int64_t resident = int64_t(num_cus) * kGroupsPerCU;  // two waves per SIMD
 
     // key ranges: requested, or automatic when the query blocks leave CUs idle
     const int64_t n_max = desc->S > 0 ? std::min<int64_t>(desc->T, (row_offset + desc->S) / m) : 0;
@@ -107,11 +111,22 @@ int make_plan(const csa_desc *desc, int32_t m, int32_t k,
     p.chunk = chunk;
     p.log_cap = k + chunk;
     p.sort_pow2 = int(next_pow2(k));
+    // rows of up to kMaxFusedSort slots are sorted at the end of the scoring
+    // kernel (no key ranges); the others by a separate pass, which needs the
+    // scores, in the workspace when the caller wants none
+#ifdef CSA_NO_FUSED_SORT
+    p.sort_e = 0;
+#else
+    p.sort_e = (p.n_splits == 1 && p.sort_pow2 <= kMaxFusedSort) ? (p.sort_pow2 <= 512 ? 8 : 32) : 0;
+#endif
+    p.no_score = no_score;
     const size_t per_wave = size_t(p.QW) * size_t(p.log_cap) * 8u;  // u32 key + i32 index
     const size_t logs = (size_t(p.grid) * kWaves * per_wave + 255) / 256 * 256;
     p.part_offset = logs;
     const size_t parts = p.n_splits > 1 ? size_t(rows) * size_t(p.n_splits) * size_t(k) * 8u : 0u;
-    p.ws_bytes = logs + (parts + 255) / 256 * 256;
+    p.score_offset = logs + (parts + 255) / 256 * 256;
+    const size_t scores = (no_score && p.sort_e == 0) ? size_t(rows) * size_t(k) * 4u : 0u;
+    p.ws_bytes = p.score_offset + (scores + 255) / 256 * 256;
     *plan = p;
     return CSA_OK;
 }

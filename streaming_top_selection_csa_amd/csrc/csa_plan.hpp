@@ -26,12 +26,18 @@
 
 namespace csa {
 
-constexpr int kWaves = 8;           // waves per workgroup (two per SIMD)
+#ifndef CSA_WAVES
+#define CSA_WAVES 8
+#endif
+constexpr int kWaves = CSA_WAVES;   // waves per workgroup
+constexpr int kGroupsPerCU = 8 / kWaves;  // resident workgroups per CU (two waves per SIMD)
 constexpr int kThreads = kWaves * 64;
 constexpr int kRowsPerWave = 64;    // (position, head) rows of q per wave
 constexpr int kKeysPerTile = 64;    // compressed keys per LDS tile
 constexpr int kMaxTopK = 16384;     // row sort holds next_pow2(k) keys in LDS
+constexpr int kMaxFusedSort = 2048; // rows up to this next_pow2(k) are sorted by the scoring kernel
 constexpr int kMaxChunk = 1 << 20;
+constexpr int64_t kMaxKeys = int64_t(1) << 30;   // largest T
 constexpr int kMinSplitKeys = 1024;              // smallest automatic key range
 constexpr size_t kMaxSplitBytes = size_t(1) << 30;  // bound of the partial lists
 
@@ -49,15 +55,19 @@ struct Plan {
     int chunk = 0;              // candidates buffered beyond k before a merge
     int log_cap = 0;            // k + chunk
     int sort_pow2 = 0;          // next power of two >= k
+    int sort_e = 0;             // > 0: the scoring kernel sorts the rows (sort_e keys per lane)
+    bool no_score = false;      // the caller passes no score output
     size_t part_offset = 0;     // byte offset of the partial lists (G > 1)
+    size_t score_offset = 0;    // byte offset of the score rows a separate sort needs
     size_t ws_bytes = 0;        // 256-aligned
 };
 
 bool supported(int dtype, int H, int D);
 
 // Validates every argument and fills `plan`.  num_cus must be > 0.
+// no_score: the call writes no scores (also implied by CSA_FLAG_NO_SCORE).
 // Returns CSA_OK or a negative csa_status; never throws.
 int make_plan(const csa_desc *desc, int32_t m, int32_t k,
-              const csa_options *opt, int num_cus, Plan *plan);
+              const csa_options *opt, int num_cus, Plan *plan, bool no_score = false);
 
 }  // namespace csa

@@ -31,6 +31,7 @@
 
 #include <cstdint>
 
+#include "csa_bitonic.hpp"
 #include "csa_kernels.hpp"
 #include "csa_order_key.hpp"
 
@@ -461,51 +462,62 @@ __device__ __noinline__ void hist_recount(uint32_t *h, int hbase, const uint32_t
     wave_lds_sync();
 }
 
-// Radix select, in LDS, of the `need` best of n candidates (cu, ci) that
-// share the top 16 bits `g` of their order keys; writes them to out[0..need)
-// (candidates kept in their LDS order, i.e. ascending key among ties).
-__device__ __forceinline__ void select_candidates(const uint32_t *cu, const int32_t *ci, int n,
-                                                  int need, uint32_t g, uint32_t *rhist,
-                                                  int32_t *oi, float *os, int lane)
+// Radix digit pick over the 256 counts in rhist: the digit d at which the
+// count from the top digit down first reaches `want` (>= 1), and in *above
+// the count in the digits above d.  Wave-uniform results.
+__device__ __forceinline__ int pick_digit(const uint32_t *rhist, uint32_t want, int lane,
+                                          uint32_t *above)
 {
-    uint32_t prefix = g << 16, pmask = 0xFFFF0000u;
+    // lane 0 owns the top digits: prefix sum over reversed digit order
+    const uint32_t r0 = rhist[255 - 4 * lane], r1 = rhist[254 - 4 * lane];
+    const uint32_t r2 = rhist[253 - 4 * lane], r3 = rhist[252 - 4 * lane];
+    const uint32_t rl = r0 + r1 + r2 + r3;
+    const uint32_t pre = wave_prefix_sum(rl);
+    const uint64_t bal = __ballot(pre >= want);
+    const int L = __ffsll(static_cast<unsigned long long>(bal)) - 1;
+    const uint32_t acc = pre - rl;
+    int d = 252 - 4 * lane;
+    uint32_t ab = acc;
+    if (acc + r0 >= want) {
+        d = 255 - 4 * lane;
+    } else if (acc + r0 + r1 >= want) {
+        d = 254 - 4 * lane;
+        ab = acc + r0;
+    } else if (acc + r0 + r1 + r2 >= want) {
+        d = 253 - 4 * lane;
+        ab = acc + r0 + r1;
+    } else {
+        ab = acc + r0 + r1 + r2;
+    }
+    *above = __builtin_amdgcn_readlane(ab, L);
+    return __builtin_amdgcn_readlane(d, L);
+}
+
+// Radix select, in LDS, of the `need` best of n candidates (cu, ci) whose
+// order keys all lie in [lo, lo + 2^shift) (shift in {0, 8, 16}); hands
+// each chosen one to put(rank, key, index), ranks 0..need-1, candidates
+// kept in their LDS order (ascending key index among ties).
+template <typename Put>
+__device__ __forceinline__ void select_candidates(const uint32_t *cu, const int32_t *ci, int n,
+                                                  int need, uint32_t lo, int shift,
+                                                  uint32_t *rhist, int lane, Put put)
+{
+    uint32_t prefix = lo, pmask = shift >= 32 ? 0u : ~((1u << shift) - 1u);
     int kk = need;
 #pragma unroll 1
-    for (int shift = 8; shift >= 0; shift -= 8) {
+    for (int sh = shift - 8; sh >= 0; sh -= 8) {
         for (int i = lane; i < 256; i += 64) rhist[i] = 0u;
         wave_lds_sync();
         for (int e = lane; e < n; e += 64) {
             const uint32_t u = cu[e];
-            if ((u & pmask) == prefix) atomicAdd(&rhist[(u >> shift) & 255u], 1u);
+            if ((u & pmask) == prefix) atomicAdd(&rhist[(u >> sh) & 255u], 1u);
         }
         wave_lds_sync();
-        // lane 0 owns the top digits: prefix sum over reversed digit order
-        const uint32_t r0 = rhist[255 - 4 * lane], r1 = rhist[254 - 4 * lane];
-        const uint32_t r2 = rhist[253 - 4 * lane], r3 = rhist[252 - 4 * lane];
-        const uint32_t rl = r0 + r1 + r2 + r3;
-        const uint32_t pre = wave_prefix_sum(rl);
-        const uint32_t want = uint32_t(kk);
-        const uint64_t bal = __ballot(pre >= want);
-        const int L = __ffsll(static_cast<unsigned long long>(bal)) - 1;
-        uint32_t acc = pre - rl;
-        int d = 252 - 4 * lane;
-        uint32_t ab = acc;
-        if (acc + r0 >= want) {
-            d = 255 - 4 * lane;
-        } else if (acc + r0 + r1 >= want) {
-            d = 254 - 4 * lane;
-            ab = acc + r0;
-        } else if (acc + r0 + r1 + r2 >= want) {
-            d = 253 - 4 * lane;
-            ab = acc + r0 + r1;
-        } else {
-            ab = acc + r0 + r1 + r2;
-        }
-        d = __builtin_amdgcn_readlane(d, L);
-        ab = __builtin_amdgcn_readlane(ab, L);
+        uint32_t ab = 0u;
+        const int d = pick_digit(rhist, uint32_t(kk), lane, &ab);
         kk -= int(ab);
-        prefix |= uint32_t(d) << shift;
-        pmask |= 0xFFu << shift;
+        prefix |= uint32_t(d) << sh;
+        pmask |= 0xFFu << sh;
         wave_lds_sync();
     }
     int wpos = 0, eq_seen = 0;
@@ -519,11 +531,7 @@ __device__ __forceinline__ void select_candidates(const uint32_t *cu, const int3
         const uint64_t meq = __ballot(eq);
         const bool keep = gt || (eq && eq_seen + lanes_below(meq) < kk);
         const uint64_t mk = __ballot(keep);
-        if (keep) {
-            const int p = wpos + lanes_below(mk);
-            oi[p] = ci[e];
-            os[p] = key_to_float(u);
-        }
+        if (keep) put(wpos + lanes_below(mk), u, ci[e]);
         wpos += __popcll(mk);
         eq_seen += __popcll(meq);
     }
@@ -601,8 +609,13 @@ __device__ __noinline__ void final_select(uint32_t *lu, int32_t *li, int cnt, in
             // the result is every entry above the bin plus the best k - wpos
             // of the bin (ties in log order, i.e. by ascending key)
             if (wpos < k && wpos + cpos >= k && cpos <= cap) {
-                select_candidates(cu, ci, cpos, k - wpos, uint32_t(g), rhist, oi + wpos,
-                                  os + wpos, lane);
+                int32_t *const oo = oi + wpos;
+                float *const so = os + wpos;
+                select_candidates(cu, ci, cpos, k - wpos, uint32_t(g) << 16, 16, rhist, lane,
+                                  [&](int p, uint32_t u, int32_t id) {
+                                      oo[p] = id;
+                                      so[p] = key_to_float(u);
+                                  });
                 wpos = k;
                 done = true;
             }
@@ -622,6 +635,254 @@ __device__ __noinline__ void final_select(uint32_t *lu, int32_t *li, int cnt, in
         oi[e] = -1;
         os[e] = -__builtin_inff();
     }
+}
+
+// ------------------------------------------------- final selection + sort
+//
+// The wave's staging area holds up to kStageSlots (order key, key index)
+// pairs in two LDS arrays; slot p lives at word stage_word(p), an XOR
+// swizzle that keeps both the blocked (lane l: slots l*E .. l*E+E-1) and the
+// striped (slot j*64 + lane) accesses of the sort on distinct banks.
+
+constexpr int kStageSlots = 2048;  // largest next_pow2(k) sorted in the scoring kernel
+
+__device__ __forceinline__ int stage_word(int p) { return p ^ ((p >> 5) & 31); }
+
+// Leaves the min(k, cnt) best entries of a position's log, in no particular
+// order, in staging slots [0, n) and returns n.  The threshold histogram
+// names the bin holding the k-th best and counts what lies above it.  While
+// that bin holds more entries than the candidate buffer, one counting pass
+// over the log narrows it by the next 8 bits of the order key.  One pass
+// then stages every entry above the range and gathers the range's entries
+// into the candidate buffer (the position's histogram words, free by then),
+// where a short radix select picks the rest; a range narrowed to a single
+// order key instead stages its first entries in log order (the lowest key
+// indices).  Falls back to the exact merge of the whole log when the bin is
+// the clamped bottom bin or the counts disagree.
+template <int NB>
+__device__ __forceinline__ int stage_select(uint32_t *lu, int32_t *li, int cnt, int k, uint32_t *h,
+                                         int hbase, uint32_t *su, uint32_t *si, uint32_t *rhist,
+                                         int lane)
+{
+    constexpr int CAP = NB / 2;  // candidate entries that fit the histogram words
+    wave_global_sync();
+    wave_lds_sync();
+    if (cnt <= k) {
+        // every log entry is a result (see the filter rule)
+#pragma unroll 1
+        for (int e = lane; e < cnt; e += 64) {
+            su[stage_word(e)] = lu[e];
+            si[stage_word(e)] = uint32_t(li[e]);
+        }
+        return cnt;
+    }
+    uint32_t above = 0u;
+    const int b = Hist<NB>::top_bin_above(h, k, lane, &above);
+    const int g = hbase + b;
+    uint32_t nb = b >= 0 ? h[b] : 0u;
+    if (b > 0 && g > 0 && g < 65535 && int(above) < k) {
+        uint32_t lo = uint32_t(g) << 16;
+        int shift = 16;  // the k-th best lies in [lo, lo + 2^shift)
+#pragma unroll 1
+        while (nb > uint32_t(CAP) && shift > 0) {
+            const uint32_t hi = lo + (1u << shift);
+            shift -= 8;
+            for (int i = lane; i < 256; i += 64) rhist[i] = 0u;
+            wave_lds_sync();
+#pragma unroll 1
+            for (int base = 0; base < cnt; base += 64 * kBatch) {
+                uint32_t u[kBatch];
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j) {
+                    const int e = base + 64 * j + lane;
+                    u[j] = e < cnt ? lu[e] : 0u;
+                }
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j)
+                    if (u[j] >= lo && u[j] < hi) atomicAdd(&rhist[(u[j] >> shift) & 255u], 1u);
+            }
+            wave_lds_sync();
+            uint32_t ab = 0u;
+            const int d = pick_digit(rhist, uint32_t(k) - above, lane, &ab);
+            above += ab;
+            nb = rhist[d];
+            lo += uint32_t(d) << shift;
+            wave_lds_sync();
+        }
+        const uint32_t hi = lo + (1u << shift);
+        const bool direct = nb > uint32_t(CAP);  // one order key left: take the first ones
+        const int need = k - int(above);
+        uint32_t *const cu = h;
+        int32_t *const ci = reinterpret_cast<int32_t *>(h + CAP);
+        int wpos = 0, cpos = 0;
+#pragma unroll 1
+        for (int base = 0; base < cnt; base += 64 * kBatch) {
+            uint32_t u[kBatch];
+            int32_t id[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const int e = base + 64 * j + lane;
+                u[j] = e < cnt ? lu[e] : 0u;
+                id[j] = e < cnt ? li[e] : 0;
+            }
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const bool valid = base + 64 * j + lane < cnt;
+                const bool sel = valid && u[j] >= hi;
+                const bool cand = valid && u[j] >= lo && u[j] < hi;
+                const uint64_t ms = __ballot(sel);
+                const uint64_t mc = __ballot(cand);
+                const int ps = wpos + lanes_below(ms);
+                const int pc = cpos + lanes_below(mc);
+                if (sel && ps < k) {
+                    su[stage_word(ps)] = u[j];
+                    si[stage_word(ps)] = uint32_t(id[j]);
+                }
+                if (cand) {
+                    if (direct) {
+                        if (pc < need) {
+                            su[stage_word(int(above) + pc)] = u[j];
+                            si[stage_word(int(above) + pc)] = uint32_t(id[j]);
+                        }
+                    } else if (pc < CAP) {
+                        cu[pc] = u[j];
+                        ci[pc] = id[j];
+                    }
+                }
+                wpos += __popcll(ms);
+                cpos += __popcll(mc);
+            }
+        }
+        wave_lds_sync();
+        if (wpos == int(above) && cpos == int(nb)) {
+            if (!direct)
+                select_candidates(cu, ci, cpos, need, lo, shift, rhist, lane,
+                                  [&](int p, uint32_t u, int32_t id) {
+                                      su[stage_word(wpos + p)] = u;
+                                      si[stage_word(wpos + p)] = uint32_t(id);
+                                  });
+            wave_lds_sync();
+            return k;
+        }
+    }
+    merge_log(lu, li, cnt, k, rhist, lane);
+#pragma unroll 1
+    for (int e = lane; e < k; e += 64) {
+        su[stage_word(e)] = lu[e];
+        si[stage_word(e)] = uint32_t(li[e]);
+    }
+    wave_lds_sync();
+    return k;
+}
+
+// Staging slots [base, base + 64*E) to registers (blocked order) as ascending
+// 64-bit keys ~orderkey << 32 | index; slots at or past n hold padding, which
+// sorts after every finite score: ~orderkey(-inf) << 32 | 0xFFFFFFFF.
+template <int E>
+__device__ __forceinline__ void load_keys(const uint32_t *su, const uint32_t *si, int base, int n,
+                                          unsigned long long (&key)[E], int lane)
+{
+    constexpr unsigned long long PAD = 0xFF800000FFFFFFFFull;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int p = base + lane * E + e;
+        const int w = stage_word(p);
+        key[e] = p < n ? (static_cast<unsigned long long>(~su[w]) << 32) | si[w] : PAD;
+    }
+}
+
+template <int E>
+__device__ __forceinline__ void store_keys(uint32_t *su, uint32_t *si, int base,
+                                           const unsigned long long (&key)[E], int lane)
+{
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int w = stage_word(base + lane * E + e);
+        si[w] = uint32_t(key[e]);
+        su[w] = ~uint32_t(key[e] >> 32);
+    }
+}
+
+// Writes sorted slots [base, base + 64*E) that lie below k to the output row
+// through the staging words (whole cache lines per store); os may be null.
+template <int E>
+__device__ __forceinline__ void write_row(uint32_t *su, uint32_t *si, int base, int k,
+                                          const unsigned long long (&key)[E], int32_t *oi,
+                                          float *os, int lane)
+{
+    wave_lds_sync();
+    store_keys<E>(su, si, base, key, lane);
+    wave_lds_sync();
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+        const int i = base + j * 64 + lane;
+        if (i < k) {
+            const int w = stage_word(i);
+            oi[i] = int32_t(si[w]);
+            if (os) os[i] = key_to_float(su[w]);
+        }
+    }
+}
+
+// Sorts staging slots [0, n) by (score desc, key index asc) and writes the
+// first k to the output row, padding (-1, -inf) after the n entries.
+// 64*E >= k slots; E <= 16 sorts in registers at once.  E = 32 sorts each
+// half of 1,024 slots in registers, joins the halves with the first step
+// of a bitonic merge on the staging words (slot i against slot 2047 - i,
+// both halves ascending), and finishes each half in registers.
+template <int E>
+__device__ __forceinline__ void sort_store(uint32_t *su, uint32_t *si, int n, int k, int32_t *oi,
+                                           float *os, int lane)
+{
+    if constexpr (E <= 16) {
+        unsigned long long key[E];
+        load_keys<E>(su, si, 0, n, key, lane);
+        bitonic_sort<E, 2>(key, lane);
+        write_row<E>(su, si, 0, k, key, oi, os, lane);
+    } else {
+        static_assert(E == 32, "one or two register passes");
+        constexpr int HE = 16, HALF = 64 * HE;
+        unsigned long long key[HE];
+#pragma unroll 1
+        for (int hf = 0; hf < 2; ++hf) {
+            load_keys<HE>(su, si, hf * HALF, n, key, lane);
+            bitonic_sort<HE, 2>(key, lane);
+            wave_lds_sync();
+            store_keys<HE>(su, si, hf * HALF, key, lane);
+            wave_lds_sync();
+        }
+#pragma unroll
+        for (int e = 0; e < HE; ++e) {
+            const int i = lane * HE + e;
+            const int wa = stage_word(i), wb = stage_word(2 * HALF - 1 - i);
+            const unsigned long long x = (static_cast<unsigned long long>(~su[wa]) << 32) | si[wa];
+            const unsigned long long y = (static_cast<unsigned long long>(~su[wb]) << 32) | si[wb];
+            if (y < x) {
+                su[wa] = ~uint32_t(y >> 32);
+                si[wa] = uint32_t(y);
+                su[wb] = ~uint32_t(x >> 32);
+                si[wb] = uint32_t(x);
+            }
+        }
+#pragma unroll 1
+        for (int hf = 0; hf < 2 && hf * HALF < k; ++hf) {
+            wave_lds_sync();
+            load_keys<HE>(su, si, hf * HALF, 2 * HALF, key, lane);
+            bitonic_step<HE, 2 * HALF, HALF / 2>(key, lane);
+            write_row<HE>(su, si, hf * HALF, k, key, oi, os, lane);
+        }
+    }
+}
+
+// The final selection of one position's log and the sort of its row (rows
+// of up to 64*E keys).
+template <int NB, int E>
+__device__ __noinline__ void final_sorted(uint32_t *lu, int32_t *li, int cnt, int k, uint32_t *h,
+                                          int hbase, uint32_t *su, uint32_t *si, uint32_t *rhist,
+                                          int32_t *oi, float *os, int lane)
+{
+    const int n = stage_select<NB>(lu, li, cnt, k, h, hbase, su, si, rhist, lane);
+    sort_store<E>(su, si, n, k, oi, os, lane);
 }
 
 // ------------------------------------------------------------ score epilogue
@@ -685,9 +946,12 @@ struct Epi {
 
 // ------------------------------------------------------------ scoring kernel
 
-// SPLIT: the launch divides the keys into a.n_splits ranges (units are
-// (query block, key range) pairs and results go to the partial lists); the
-// plain instantiation keeps every key range at [0, n_vis).
+// SPLIT: units are (query block, key range) pairs, a.n_splits ranges of
+// a.split_keys keys (one range of all keys when n_splits = 1), and each unit
+// leaves the top-k of its range unsorted in a list (a partial list, or the
+// output row itself with one range) for the merge and sort passes.
+// Otherwise units are query blocks and each row leaves the kernel sorted
+// (next_pow2(k) <= kStageSlots).
 template <int H, int D, bool FP8, bool SPLIT>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 stream_topk_kernel(StreamArgs a)
@@ -712,10 +976,22 @@ stream_topk_kernel(StreamArgs a)
     // trips and a wave scan, a looser threshold only some extra appends
     constexpr int UPD = 512;
 
-    __shared__ __attribute__((aligned(16))) unsigned char s_k[NBUF][TILEB];
-    __shared__ float s_ks[NBUF][KT];
-    __shared__ uint32_t s_rhist[kWaves][256];       // radix select scratch
-    __shared__ uint32_t s_th[kWaves][QW * NB];      // threshold histograms
+    // the key ring, and after a block's last tile each wave's staging area
+    // for the final selection and sort (two arrays of kStageSlots words)
+    constexpr int STAGEB = 2 * kStageSlots * 4;
+    constexpr int UNIONB = NBUF * TILEB > kWaves * STAGEB ? NBUF * TILEB : kWaves * STAGEB;
+    // One LDS block, laid out by hand: the small arrays the filter and the
+    // selection hit on every tile first (lowest addresses), then the ring.
+    constexpr int THB = kWaves * QW * NB * 4;       // threshold histograms
+    constexpr int RHB = kWaves * 256 * 4;           // radix select scratch
+    constexpr int KSB = (NBUF * KT * 4 + 15) / 16 * 16;  // fp8 key scales of the ring
+    constexpr int UOFF = THB + RHB + KSB;
+    __shared__ __attribute__((aligned(16))) unsigned char s_lds[UOFF + UNIONB];
+    uint32_t (*const s_th)[QW * NB] = reinterpret_cast<uint32_t (*)[QW * NB]>(s_lds);
+    uint32_t (*const s_rhist)[256] = reinterpret_cast<uint32_t (*)[256]>(s_lds + THB);
+    float (*const s_ks)[KT] = reinterpret_cast<float (*)[KT]>(s_lds + THB + RHB);
+    unsigned char *const s_union = s_lds + UOFF;
+    unsigned char (*const s_k)[TILEB] = reinterpret_cast<unsigned char (*)[TILEB]>(s_union);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -979,9 +1255,14 @@ stream_topk_kernel(StreamArgs a)
             // leading and the lagging waves issue their loads half a tile
             // apart.
             const bool stage = it + PD < ntiles;
+            // The epilogue of one half tile is issued before the next half's
+            // MFMAs (a scheduling barrier), so both halves share one set of
+            // accumulator registers: the other wave of the SIMD keeps the
+            // matrix core busy meanwhile.
             if (!lagging) {
                 mma_half(buf, 0);
                 E::partial(acc, wr, h0);
+                __builtin_amdgcn_sched_barrier(0);
                 mma_half(buf, 1);
                 E::partial(acc, wr, h1);
                 finish(h0, h1, it, ksv);
@@ -989,11 +1270,13 @@ stream_topk_kernel(StreamArgs a)
             } else {
                 if (it > 0) {
                     E::partial(acc, wr, h1);
+                    __builtin_amdgcn_sched_barrier(0);
                     finish(h0, h1, it - 1, ksv_prev);
                 }
                 if (stage) dma_tile(it + PD, (it + PD) % NBUF);
                 mma_half(buf, 0);
                 E::partial(acc, wr, h0);
+                __builtin_amdgcn_sched_barrier(0);
                 mma_half(buf, 1);
             }
             ksv_prev = ksv;
@@ -1004,11 +1287,32 @@ stream_topk_kernel(StreamArgs a)
             finish(h0, h1, ntiles - 1, ksv_prev);
         }
 
-        // ---- final selection into the (unsorted) output rows; the key ring
-        // is idle until the next block's first barrier and serves as each
-        // wave's candidate buffer
+        // ---- final selection.  The key ring is idle until the next block's
+        // first barrier: it serves as each wave's staging area (sorted rows)
+        // or candidate buffer (unsorted rows, sorted by a later pass).
+        if constexpr (!SPLIT) {
+            uint32_t *const su = reinterpret_cast<uint32_t *>(s_union + wave * STAGEB);
+            uint32_t *const si = su + kStageSlots;
+#pragma unroll 1
+            for (int qi = 0; qi < QW; ++qi) {
+                const int64_t pos = wp0 + qi;
+                if (pos >= a.S) break;
+                const int64_t row = (b * a.S + pos) * a.topk;
+                int32_t *const oi = a.out_idx + row;
+                float *const os = a.out_score ? a.out_score + row : nullptr;
+                if (a.sort_e <= 8)
+                    final_sorted<NB, 8>(log_u + qi * a.log_cap, log_i + qi * a.log_cap, cnt[qi],
+                                        a.topk, &s_th[wave][qi * NB], hbase[qi], su, si, rhist,
+                                        oi, os, lane);
+                else
+                    final_sorted<NB, 32>(log_u + qi * a.log_cap, log_i + qi * a.log_cap, cnt[qi],
+                                         a.topk, &s_th[wave][qi * NB], hbase[qi], su, si, rhist,
+                                         oi, os, lane);
+            }
+            continue;
+        }
         constexpr int CAP = NBUF * TILEB / kWaves / 8;
-        uint32_t *const cu = reinterpret_cast<uint32_t *>(&s_k[0][0] + wave * (NBUF * TILEB / kWaves));
+        uint32_t *const cu = reinterpret_cast<uint32_t *>(s_union + wave * (NBUF * TILEB / kWaves));
         int32_t *const ci = reinterpret_cast<int32_t *>(cu + CAP);
 #pragma unroll 1
         for (int qi = 0; qi < QW; ++qi) {
@@ -1029,7 +1333,7 @@ stream_topk_kernel(StreamArgs a)
 template <int H, int D, bool FP8>
 static hipError_t launch_one(const StreamArgs &a, int grid, hipStream_t s)
 {
-    if (a.n_splits > 1)
+    if (a.sort_e == 0)
         hipLaunchKernelGGL((stream_topk_kernel<H, D, FP8, true>), dim3(grid), dim3(kThreads), 0,
                            s, a);
     else

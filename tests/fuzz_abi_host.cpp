@@ -99,7 +99,7 @@ int main(int argc, char **argv)
         o.num_cus = (rng() % 4 == 0) ? 0 : 1 + int32_t(rng() % 512);
         o.row_offset = pick64();
         o.key_splits = (rng() % 3 == 0) ? pick32() : 0;
-        o.reserved1 = (rng() % 16 == 0) ? 2 : 0;
+        o.flags = int32_t(rng() % 16 == 0 ? 2 : rng() % 4 == 0 ? CSA_FLAG_NO_SCORE : 0);
         o.workspace = (rng() & 1) ? p : nullptr;
         o.workspace_bytes = size_t(rng() % (size_t(1) << 34));
         const int32_t m = pick32(), k = pick32();

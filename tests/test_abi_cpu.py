@@ -125,7 +125,10 @@ def test_index_rejects_before_touching_the_device(lib):
     assert call_index(lib, w=None) == B.CSA_ERR_INVALID_ARG
     assert call_index(lib, k_cmp=None) == B.CSA_ERR_INVALID_ARG
     assert call_index(lib, oi=None) == B.CSA_ERR_INVALID_ARG
-    assert call_index(lib, os_=None) == B.CSA_ERR_INVALID_ARG
+    # out_score = NULL is valid (no scores returned): it gets as far as the
+    # workspace check, still before any device work
+    assert call_index(lib, os_=None, opt=opts(workspace=256, workspace_bytes=1024)) == \
+        B.CSA_ERR_WORKSPACE
     assert call_index(lib, q=24) == B.CSA_ERR_INVALID_ARG          # q not 16-byte aligned
     assert call_index(lib, k_cmp=40) == B.CSA_ERR_INVALID_ARG
     assert call_index(lib, w=18) == B.CSA_ERR_INVALID_ARG
@@ -181,7 +184,7 @@ def test_key_splits_validation(lib):
     ok = csa.make_desc(1, 100, 25, 64, 128)
     assert bad(lib, ok, opt=opts(key_splits=-1)) == B.CSA_ERR_INVALID_ARG
     o = opts()
-    o.reserved1 = 3
+    o.flags = 3
     assert bad(lib, ok, opt=o) == B.CSA_ERR_INVALID_ARG
 
 
@@ -354,3 +357,29 @@ def test_host_code_fuzz_under_sanitizers(tmp_path):
                          env=env)
     assert res.returncode == 0, (res.stdout + res.stderr)[-3000:]
     assert "fuzz ok" in res.stdout
+
+
+def test_no_score_workspace_sizes(lib):
+    """CSA_FLAG_NO_SCORE sizes the workspace for out_score = NULL: nothing
+    extra when the scoring kernel sorts the rows (next_pow2(k) <= 2048, no
+    key ranges), B*S*k*4 more bytes when a separate pass sorts them."""
+    d = csa.make_desc(1, 100000, 25000, 64, 128)
+    ns = opts(flags=csa.CSA_FLAG_NO_SCORE)
+    assert csa.workspace_bytes(d, 4, 2048, ns) == csa.workspace_bytes(d, 4, 2048, opts())
+    assert (csa.workspace_bytes(d, 4, 4096, ns) - csa.workspace_bytes(d, 4, 4096, opts())
+            == 100000 * 4096 * 4)
+    few = csa.make_desc(1, 64, 65536, 64, 128)
+    o = opts(row_offset=262080, key_splits=8)
+    o_ns = opts(row_offset=262080, key_splits=8, flags=csa.CSA_FLAG_NO_SCORE)
+    assert csa.workspace_bytes(few, 4, 2048, o_ns) - csa.workspace_bytes(few, 4, 2048, o) == \
+        64 * 2048 * 4
+    # other flag bits are invalid
+    assert csa.workspace_bytes(d, 4, 2048, opts(flags=2)) == 0
+
+
+def test_key_count_bound(lib):
+    """T is limited to 2^30 compressed keys (the kernels' key arithmetic is
+    32-bit)."""
+    ok = csa.make_desc(1, 16, 1 << 30, 64, 128)
+    assert csa.plan_query(ok, 4, 16, opts()).grid >= 1
+    assert bad(lib, csa.make_desc(1, 16, (1 << 30) + 1, 64, 128)) == B.CSA_ERR_INVALID_ARG
