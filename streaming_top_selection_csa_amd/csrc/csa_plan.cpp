@@ -83,7 +83,7 @@ int make_plan(const csa_desc *desc, int32_t m, int32_t k,
     p.QB = kWaves * p.QW;
     p.blocks_per_batch = (desc->S + p.QB - 1) / p.QB;
     p.n_blocks = p.blocks_per_batch * desc->B;
-    const int64_t resident = int64_t(num_cus) * kGroupsPerCU;  // two waves per SIMD
+    const int64_t resident = int64_t(num_cus);  // one 8-wave workgroup per CU
 
     // key ranges: requested, or automatic when the query blocks leave CUs idle
     const int64_t n_max = desc->S > 0 ? std::min<int64_t>(desc->T, (row_offset + desc->S) / m) : 0;
@@ -114,11 +114,7 @@ int make_plan(const csa_desc *desc, int32_t m, int32_t k,
     // rows of up to kMaxFusedSort slots are sorted at the end of the scoring
     // kernel (no key ranges); the others by a separate pass, which needs the
     // scores, in the workspace when the caller wants none
-#ifdef CSA_NO_FUSED_SORT
-    p.sort_e = 0;
-#else
     p.sort_e = (p.n_splits == 1 && p.sort_pow2 <= kMaxFusedSort) ? (p.sort_pow2 <= 512 ? 8 : 32) : 0;
-#endif
     p.no_score = no_score;
     const size_t per_wave = size_t(p.QW) * size_t(p.log_cap) * 8u;  // u32 key + i32 index
     const size_t logs = (size_t(p.grid) * kWaves * per_wave + 255) / 256 * 256;

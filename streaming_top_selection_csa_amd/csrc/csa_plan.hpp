@@ -26,11 +26,7 @@
 
 namespace csa {
 
-#ifndef CSA_WAVES
-#define CSA_WAVES 8
-#endif
-constexpr int kWaves = CSA_WAVES;   // waves per workgroup
-constexpr int kGroupsPerCU = 8 / kWaves;  // resident workgroups per CU (two waves per SIMD)
+constexpr int kWaves = 8;           // waves per workgroup (two per SIMD, one workgroup per CU)
 constexpr int kThreads = kWaves * 64;
 constexpr int kRowsPerWave = 64;    // (position, head) rows of q per wave
 constexpr int kKeysPerTile = 64;    // compressed keys per LDS tile
