@@ -174,6 +174,30 @@ int csa_index_ex(const void *q, const float *w, const void *k_cmp,
 size_t csa_workspace_bytes(const csa_desc *desc, int32_t m, int32_t k,
                            const csa_options *opt);
 
+/*
+ * csa_index_static: csa_index_ex without any allocation, for callers that
+ * cannot allocate device memory (code under graph capture, tight serving
+ * loops, hosts that forbid allocation).  Same arguments, results and errors
+ * as csa_index_ex, except:
+ *   - opt->workspace must be NULL and opt->workspace_bytes 0
+ *     (CSA_ERR_INVALID_ARG otherwise): the scratch is a fixed array of
+ *     CSA_STATIC_SCRATCH_BYTES bytes in device memory, one per GPU, held from
+ *     the library's load until the process ends;
+ *   - with chunk_keys = 0 the partition size is lowered (halved, down to 64)
+ *     until the call's workspace fits that array; a call that still needs
+ *     more returns CSA_ERR_WORKSPACE before anything is launched.
+ * It makes no hipMalloc, hipFree or other allocating call.  Every call on a
+ * GPU uses that GPU's one array (nothing in it needs to start cleared):
+ * calls that may overlap on one GPU (other streams, other host threads)
+ * race and must be serialised by the caller.
+ */
+#define CSA_STATIC_SCRATCH_BYTES (128u << 20)
+
+int csa_index_static(const void *q, const float *w, const void *k_cmp,
+                     const csa_desc *desc, int32_t m, int32_t k,
+                     int32_t *out_idx, float *out_score,
+                     const csa_options *opt, hipStream_t stream);
+
 /* Host-only planning: validates the arguments and reports the launch plan.
  * Makes no HIP call when opt->num_cus > 0. */
 int csa_plan_query(const csa_desc *desc, int32_t m, int32_t k,

@@ -29,7 +29,7 @@ CSA_FP8_E4M3FN = 1
 
 CSA_FLAG_NO_SCORE = 1
 
-EXPORTS = ("csa_index", "csa_index_ex", "csa_workspace_bytes", "csa_plan_query",
+EXPORTS = ("csa_index", "csa_index_ex", "csa_index_static", "csa_workspace_bytes", "csa_plan_query",
            "csa_status_string", "csa_sparse_attention", "csa_sparse_attention_ex",
            "csa_sparse_attention_workspace_bytes")
 
@@ -91,6 +91,8 @@ def load_library():
     lib.csa_index_ex.argtypes = [vp, vp, vp, ctypes.POINTER(CsaDesc), i32, i32, vp, vp,
                                  ctypes.POINTER(CsaOptions), vp]
     lib.csa_index_ex.restype = ctypes.c_int
+    lib.csa_index_static.argtypes = lib.csa_index_ex.argtypes
+    lib.csa_index_static.restype = ctypes.c_int
     lib.csa_workspace_bytes.argtypes = [ctypes.POINTER(CsaDesc), i32, i32,
                                         ctypes.POINTER(CsaOptions)]
     lib.csa_workspace_bytes.restype = ctypes.c_size_t
@@ -147,6 +149,9 @@ def plan_query(desc: CsaDesc, m: int, k: int, opt: Optional[CsaOptions] = None) 
     return info
 
 
+STATIC_SCRATCH_BYTES = 128 << 20   # CSA_STATIC_SCRATCH_BYTES
+
+
 def workspace_bytes(desc: CsaDesc, m: int, k: int, opt: Optional[CsaOptions] = None) -> int:
     return int(load_library().csa_workspace_bytes(
         ctypes.byref(desc), int(m), int(k), ctypes.byref(opt) if opt is not None else None))
@@ -174,8 +179,11 @@ def index(q: torch.Tensor, w: torch.Tensor, k_cmp: torch.Tensor, m: int, k: int,
           out_idx: Optional[torch.Tensor] = None, out_score: Optional[torch.Tensor] = None,
           chunk_keys: int = 0, row_offset: int = 0, key_splits: int = 0,
           workspace: Optional[torch.Tensor] = None, timing=None,
-          stream: Optional[torch.cuda.Stream] = None, want_score: bool = True):
-    """Top-k compressed keys per query position (csa_index_ex).
+          stream: Optional[torch.cuda.Stream] = None, want_score: bool = True,
+          static_scratch: bool = False):
+    """Top-k compressed keys per query position (csa_index_ex, or with
+    static_scratch=True csa_index_static: no allocation, the library's fixed
+    device scratch instead of a workspace; `workspace` must then be None).
 
     q [B,S,H,D] bf16 | e4m3fn, w [B,S,H] fp32, k_cmp [B,T,D] same dtype as
     q; for fp8 also q_scale [B,S,H] and k_scale [B,T] fp32.  Returns
@@ -230,12 +238,13 @@ def index(q: torch.Tensor, w: torch.Tensor, k_cmp: torch.Tensor, m: int, k: int,
                        timing if timing is not None else (None, None), key_splits)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    rc = lib.csa_index_ex(q.data_ptr(), w.data_ptr(), k_cmp.data_ptr(), ctypes.byref(desc),
-                          int(m), int(k), out_idx.data_ptr(),
-                          out_score.data_ptr() if out_score is not None else None,
-                          ctypes.byref(opt), ctypes.c_void_p(stream.cuda_stream))
+    fn = lib.csa_index_static if static_scratch else lib.csa_index_ex
+    rc = fn(q.data_ptr(), w.data_ptr(), k_cmp.data_ptr(), ctypes.byref(desc),
+            int(m), int(k), out_idx.data_ptr(),
+            out_score.data_ptr() if out_score is not None else None,
+            ctypes.byref(opt), ctypes.c_void_p(stream.cuda_stream))
     if rc != CSA_OK:
-        raise CsaError(rc, "csa_index_ex")
+        raise CsaError(rc, "csa_index_static" if static_scratch else "csa_index_ex")
     return out_idx, out_score
 
 

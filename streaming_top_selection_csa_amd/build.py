@@ -19,7 +19,7 @@ OBJDIR = os.path.join(HERE, "_build")
 # the scoring-kernel instantiations first: they take longest
 SOURCES = ["csa_stream_bf16_d128.hip", "csa_stream_fp8_d128.hip", "csa_stream_bf16_d64.hip",
            "csa_stream_fp8_d64.hip", "csa_stream_bf16_d32.hip", "csa_kernels.hip", "csa_attn.hip",
-           "csa_sort.hip", "csa_plan.cpp", "csa_abi.cpp"]
+           "csa_sort.hip", "csa_plan.cpp", "csa_abi.cpp", "csa_static.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -383,3 +383,19 @@ def test_key_count_bound(lib):
     ok = csa.make_desc(1, 16, 1 << 30, 64, 128)
     assert csa.plan_query(ok, 4, 16, opts()).grid >= 1
     assert bad(lib, csa.make_desc(1, 16, (1 << 30) + 1, 64, 128)) == B.CSA_ERR_INVALID_ARG
+
+
+def test_static_entry_point_validation(lib):
+    """csa_index_static rejects a caller workspace and a call whose
+    workspace cannot fit its fixed scratch, before touching the device."""
+    d = csa.make_desc(1, 100, 25, 64, 128)
+    o = opts(workspace=256, workspace_bytes=1 << 20)
+    assert lib.csa_index_static(16, 16, 16, ctypes.byref(d), 4, 8, 16, 16, ctypes.byref(o),
+                                None) == B.CSA_ERR_INVALID_ARG
+    # k = 16,384 rows: candidate logs of 256 * 8 * (16,384 + 64) * 8 bytes even
+    # at the smallest partition, more than the 128 MiB scratch
+    big = csa.make_desc(1, 1 << 20, 1 << 18, 64, 128)
+    assert lib.csa_index_static(16, 16, 16, ctypes.byref(big), 4, 16384, 16, 16,
+                                ctypes.byref(opts()), None) == B.CSA_ERR_WORKSPACE
+    assert lib.csa_index_static(16, 16, 16, ctypes.byref(d), 0, 8, 16, 16,
+                                ctypes.byref(opts()), None) == B.CSA_ERR_INVALID_ARG
