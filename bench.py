@@ -236,31 +236,42 @@ def attention(csa, args):
 
 
 def sweep(csa, args):
-    """Chunk-size and top-k sweeps on the S=65,536 workload.  Each cell is
-    `warmup` untimed calls and `steps` timed ones on resident inputs."""
+    """The S=65,536 workload's five-point sweeps: candidate-log partition
+    (chunk_keys), top-k, keys staged per LDS tile (key_tile) and keys per
+    key range (the T keys cut into ranges whose exact top-k lists a merge
+    pass combines).  Each cell is `warmup` untimed calls and `steps` timed
+    ones on resident inputs; scoring_kernel_ms covers the scoring kernel,
+    ms_per_step the whole call (with ranges: also the merge and sort)."""
     import torch
-    from csa_synth import CHUNK_SWEEP, TOPK_SWEEP, WORKLOADS, make_inputs
+    from csa_synth import (CHUNK_SWEEP, KEY_TILE_SWEEP, RANGE_SWEEP, TOPK_SWEEP, WORKLOADS,
+                           make_inputs)
 
     base = WORKLOADS["s64k"]
     dev = torch.device("cuda:0")
     inp = make_inputs(base, seed=0, device=dev)
-    cells = [("chunk_keys", c, base.k) for c in CHUNK_SWEEP] + \
-            [("topk", base.k, k) for k in TOPK_SWEEP]
+    cells = [("chunk_keys", dict(chunk_keys=c), base.k) for c in CHUNK_SWEEP] + \
+            [("topk", {}, k) for k in TOPK_SWEEP] + \
+            [("key_tile", dict(key_tile=t), base.k) for t in KEY_TILE_SWEEP] + \
+            [("range_keys", dict(key_splits=base.n_keys // r), base.k) for r in RANGE_SWEEP]
+    axes = set(args.sweep_axes.split(",")) if args.sweep_axes else None
     flops = 2.0 * base.H * base.D * visible_pairs(base.S, base.n_keys, base.m, base.B)
     stream = torch.cuda.current_stream(dev)
-    for axis, chunk, k in cells:
-        c = chunk if axis == "chunk_keys" else 0
+    for axis, kw, k in cells:
+        if axes is not None and axis not in axes:
+            continue
+        c = kw.get("chunk_keys", 0)
+        G = kw.get("key_splits", 0)
         out_idx = torch.empty((base.B, base.S, k), dtype=torch.int32, device=dev)
         out_score = torch.empty((base.B, base.S, k), dtype=torch.float32, device=dev)
-        ws = csa.workspace_for(inp["q"], inp["k"], base.m, k, c)
+        ws = csa.workspace_for(inp["q"], inp["k"], base.m, k, c, key_splits=G)
         info = csa.plan_query(csa.make_desc(base.B, base.S, base.n_keys, base.H, base.D), base.m,
-                              k, csa.make_options(chunk_keys=c, num_cus=256))
+                              k, csa.make_options(chunk_keys=c, num_cus=256, key_splits=G,
+                                                  key_tile=kw.get("key_tile", 0)))
         events = csa.HipEvents(args.steps)
 
         def step(timing=None):
             csa.index(inp["q"], inp["w"], inp["k"], base.m, k, out_idx=out_idx,
-                      out_score=out_score, chunk_keys=c, workspace=ws, timing=timing,
-                      stream=stream)
+                      out_score=out_score, workspace=ws, timing=timing, stream=stream, **kw)
 
         for _ in range(args.warmup):
             step()
@@ -274,7 +285,9 @@ def sweep(csa, args):
         events.close()
         print(json.dumps({
             "sweep": axis, "workload": base.name, "S": base.S, "T": base.n_keys,
-            "chunk_keys": info.chunk_keys, "k": k, "steps": args.steps,
+            "chunk_keys": info.chunk_keys, "k": k, "key_tile": info.keys_per_tile,
+            "key_ranges": info.key_splits,
+            "range_keys": -(-base.n_keys // info.key_splits), "steps": args.steps,
             "ms_per_step": 1e3 * elapsed / args.steps, "scoring_kernel_ms": kms,
             "queries_per_s": base.B * base.S * args.steps / elapsed,
             "scoring_tflops": flops / (kms * 1e-3) / 1e12,
@@ -294,9 +307,12 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
-                    help="time the five chunk sizes (k=2048) and the five top-k values "
-                         "(default chunk) on the S=65,536 workload, one JSON line per cell; "
+                    help="time the five-point sweeps of the S=65,536 workload (chunk size, "
+                         "top-k, staged key tile, key-range size), one JSON line per cell; "
                          "the GPU tests check every cell against the oracle")
+    ap.add_argument("--sweep-axes", default="",
+                    help="with --sweep: comma-separated subset of chunk_keys,topk,key_tile,"
+                         "range_keys")
     ap.add_argument("--entry-splits", type=int, default=0,
                     help="with an attn-* workload: ranges per row of the attention (0 = "
                          "automatic, 1 = none)")

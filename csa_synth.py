@@ -80,6 +80,10 @@ WORKLOADS = {
 # workload, five points around its defaults (chunk 8192, k 2048)
 CHUNK_SWEEP = (1024, 2048, 4096, 8192, 16384)
 TOPK_SWEEP = (256, 512, 1024, 2048, 4096)
+# keys staged per LDS tile, and keys per key range (the partition of the T
+# keys whose exact top-k lists are merged), on the same workload
+KEY_TILE_SWEEP = (32, 64, 128, 192, 256)
+RANGE_SWEEP = (1024, 2048, 4096, 8192, 16384)
 
 
 def _generator(device, seed: int, stream: int) -> torch.Generator:

@@ -108,12 +108,21 @@ typedef struct {
  *                ranges of at least max(2k, 1024) keys to fill it (short query
  *                blocks, decode steps).  n >= 1 asks for n ranges (at most one
  *                per 64 visible keys).  The partial lists take B*S*G*k*8
- *                bytes of workspace, capped at 1 GiB by lowering G.  Affects
- *                speed and workspace only, never the result.
+ *                bytes of workspace: an automatic G is lowered to keep them
+ *                under 1 GiB, a requested one under 64 GiB.  Affects speed
+ *                and workspace only, never the result.
  *   flags        0, or CSA_FLAG_NO_SCORE: the call will pass out_score = NULL.
  *                Only csa_workspace_bytes and csa_plan_query read it (a call
  *                with out_score = NULL plans for that by itself); other bits
  *                must be 0.
+ *   key_tile     Compressed keys staged in LDS per workgroup step (one
+ *                barrier each); 0 = the default: 128 for H = 64, D = 128
+ *                rows sorted by the scoring kernel (next_pow2(k) <= 2048,
+ *                one key range), else 64.  64 works everywhere; 32, 128,
+ *                192 and 256 (bf16) and 128 (fp8) are built for such
+ *                H = 64, D = 128 calls only and return CSA_ERR_UNSUPPORTED
+ *                elsewhere.  Affects speed only, never the result.
+ *   reserved2    Must be 0.
  */
 typedef struct {
     int32_t chunk_keys;
@@ -124,6 +133,8 @@ typedef struct {
     hipEvent_t timing[2];
     int32_t key_splits;
     int32_t flags;
+    int32_t key_tile;
+    int32_t reserved2;
 } csa_options;
 
 /* csa_options.flags: size the workspace for calls without a score output. */

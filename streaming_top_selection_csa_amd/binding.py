@@ -45,7 +45,8 @@ class CsaOptions(ctypes.Structure):
     _fields_ = [("chunk_keys", ctypes.c_int32), ("num_cus", ctypes.c_int32),
                 ("row_offset", ctypes.c_int64), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t), ("timing", ctypes.c_void_p * 2),
-                ("key_splits", ctypes.c_int32), ("flags", ctypes.c_int32)]
+                ("key_splits", ctypes.c_int32), ("flags", ctypes.c_int32),
+                ("key_tile", ctypes.c_int32), ("reserved2", ctypes.c_int32)]
 
 
 class CsaPlanInfo(ctypes.Structure):
@@ -125,8 +126,9 @@ def make_desc(B, S, T, H, D, dtype=CSA_BF16, q_scale_ptr=0, k_scale_ptr=0) -> Cs
 
 
 def make_options(chunk_keys=0, row_offset=0, num_cus=0, workspace=None, workspace_bytes=0,
-                 timing=(None, None), key_splits=0, flags=0) -> CsaOptions:
+                 timing=(None, None), key_splits=0, flags=0, key_tile=0) -> CsaOptions:
     opt = CsaOptions()
+    opt.key_tile = int(key_tile)
     opt.key_splits = int(key_splits)
     opt.flags = int(flags)
     opt.chunk_keys = int(chunk_keys)
@@ -180,7 +182,7 @@ def index(q: torch.Tensor, w: torch.Tensor, k_cmp: torch.Tensor, m: int, k: int,
           chunk_keys: int = 0, row_offset: int = 0, key_splits: int = 0,
           workspace: Optional[torch.Tensor] = None, timing=None,
           stream: Optional[torch.cuda.Stream] = None, want_score: bool = True,
-          static_scratch: bool = False):
+          static_scratch: bool = False, key_tile: int = 0):
     """Top-k compressed keys per query position (csa_index_ex, or with
     static_scratch=True csa_index_static: no allocation, the library's fixed
     device scratch instead of a workspace; `workspace` must then be None).
@@ -235,7 +237,8 @@ def index(q: torch.Tensor, w: torch.Tensor, k_cmp: torch.Tensor, m: int, k: int,
         _check(workspace, "workspace")
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     opt = make_options(chunk_keys, row_offset, 0, ws_ptr, ws_bytes,
-                       timing if timing is not None else (None, None), key_splits)
+                       timing if timing is not None else (None, None), key_splits,
+                       key_tile=key_tile)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     fn = lib.csa_index_static if static_scratch else lib.csa_index_ex

@@ -69,7 +69,7 @@ extern "C" int csa_plan_query(const csa_desc *desc, int32_t m, int32_t k,
     const int rc = plan_for(desc, m, k, opt, &p, &cus);
     if (rc != CSA_OK) return rc;
     out->queries_per_block = p.QB;
-    out->keys_per_tile = csa::kKeysPerTile;
+    out->keys_per_tile = p.key_tile;
     out->chunk_keys = p.chunk;
     out->log_capacity = p.log_cap;
     out->grid = p.grid;
@@ -148,6 +148,7 @@ extern "C" int csa_index_ex(const void *q, const float *w, const void *k_cmp,
     a.blocks_per_batch = p.blocks_per_batch;
     a.n_units = p.n_units;
     a.sort_e = p.sort_e;
+    a.key_tile = p.key_tile;
 
     rc = CSA_OK;
     if (opt && opt->timing[0] && hipEventRecord(opt->timing[0], stream) != hipSuccess)

@@ -26,6 +26,7 @@ struct StreamArgs {
     int n_splits, split_keys;   // G key ranges of split_keys keys (G = 1: all keys)
     int64_t blocks_per_batch, n_units;
     int sort_e;                 // > 0: rows sorted in the kernel, sort_e keys per lane
+    int key_tile;               // keys staged in LDS per workgroup step
 };
 
 hipError_t launch_stream_topk(const Plan &p, const StreamArgs &a, hipStream_t s);

@@ -15,6 +15,21 @@ bool supported(int dtype, int H, int D)
     return false;
 }
 
+bool key_tile_supported(int key_tile, int dtype, int H, int D)
+{
+    if (key_tile == kKeysPerTile) return true;
+    if (H != 64 || D != 128) return false;
+    if (dtype == CSA_FP8_E4M3FN) return key_tile == 128;
+    return key_tile == 32 || key_tile == 128 || key_tile == 192 || key_tile == 256;
+}
+
+int default_key_tile(int H, int D)
+{
+    // two 64-key compute tiles per staged tile halve the workgroup barriers
+    // (measured faster at H_I = 64, d_I = 128)
+    return H == 64 && D == 128 ? 128 : kKeysPerTile;
+}
+
 static int64_t next_pow2(int64_t x)
 {
     int64_t p = 1;
@@ -43,7 +58,10 @@ int make_plan(const csa_desc *desc, int32_t m, int32_t k,
     int64_t row_offset = 0;
     int chunk = 0;
     int splits_req = 0;
+    int key_tile = 0;
     if (opt) {
+        if (opt->reserved2 != 0 || opt->key_tile < 0) return CSA_ERR_INVALID_ARG;
+        key_tile = opt->key_tile;
         if (opt->row_offset < 0 || opt->chunk_keys < 0 || opt->chunk_keys > kMaxChunk)
             return CSA_ERR_INVALID_ARG;
         if (opt->key_splits < 0 || (opt->flags & ~int32_t(CSA_FLAG_NO_SCORE)) != 0)
@@ -97,7 +115,10 @@ int make_plan(const csa_desc *desc, int32_t m, int32_t k,
         const int64_t min_keys = std::max<int64_t>(int64_t(2) * k, kMinSplitKeys);
         G = std::min<int64_t>((resident + p.n_blocks - 1) / p.n_blocks, n_max / min_keys);
     }
-    const int64_t g_cap = int64_t(kMaxSplitBytes / (size_t(rows > 0 ? rows : 1) * size_t(k) * 8u));
+    // the partial lists take rows*G*k*8 bytes: an automatic G keeps them
+    // under 1 GiB, a requested one under 64 GiB
+    const size_t list_cap = splits_req > 0 ? kMaxSplitBytesRequested : kMaxSplitBytes;
+    const int64_t g_cap = int64_t(list_cap / (size_t(rows > 0 ? rows : 1) * size_t(k) * 8u));
     G = std::max<int64_t>(1, std::min(G, g_cap));
     if (G > 1) {
         const int64_t per = (n_max + G - 1) / G;
@@ -115,6 +136,12 @@ int make_plan(const csa_desc *desc, int32_t m, int32_t k,
     // kernel (no key ranges); the others by a separate pass, which needs the
     // scores, in the workspace when the caller wants none
     p.sort_e = (p.n_splits == 1 && p.sort_pow2 <= kMaxFusedSort) ? (p.sort_pow2 <= 512 ? 8 : 32) : 0;
+    // other key tiles exist for the sorted-row kernel only
+    if (key_tile == 0) key_tile = p.sort_e > 0 ? default_key_tile(desc->H, desc->D) : kKeysPerTile;
+    if (key_tile != kKeysPerTile &&
+        (!key_tile_supported(key_tile, desc->dtype, desc->H, desc->D) || p.sort_e == 0))
+        return CSA_ERR_UNSUPPORTED;
+    p.key_tile = key_tile;
     p.no_score = no_score;
     const size_t per_wave = size_t(p.QW) * size_t(p.log_cap) * 8u;  // u32 key + i32 index
     const size_t logs = (size_t(p.grid) * kWaves * per_wave + 255) / 256 * 256;

@@ -29,13 +29,14 @@ namespace csa {
 constexpr int kWaves = 8;           // waves per workgroup (two per SIMD, one workgroup per CU)
 constexpr int kThreads = kWaves * 64;
 constexpr int kRowsPerWave = 64;    // (position, head) rows of q per wave
-constexpr int kKeysPerTile = 64;    // compressed keys per LDS tile
+constexpr int kKeysPerTile = 64;    // compressed keys per compute tile (one key per lane)
 constexpr int kMaxTopK = 16384;     // row sort holds next_pow2(k) keys in LDS
 constexpr int kMaxFusedSort = 2048; // rows up to this next_pow2(k) are sorted by the scoring kernel
 constexpr int kMaxChunk = 1 << 20;
 constexpr int64_t kMaxKeys = int64_t(1) << 30;   // largest T
 constexpr int kMinSplitKeys = 1024;              // smallest automatic key range
-constexpr size_t kMaxSplitBytes = size_t(1) << 30;  // bound of the partial lists
+constexpr size_t kMaxSplitBytes = size_t(1) << 30;  // bound of the partial lists (automatic G)
+constexpr size_t kMaxSplitBytesRequested = size_t(1) << 36;  // same, G set by the caller
 
 struct Plan {
     int64_t B = 0, S = 0, T = 0, row_offset = 0;
@@ -52,6 +53,7 @@ struct Plan {
     int log_cap = 0;            // k + chunk
     int sort_pow2 = 0;          // next power of two >= k
     int sort_e = 0;             // > 0: the scoring kernel sorts the rows (sort_e keys per lane)
+    int key_tile = kKeysPerTile;  // keys staged in LDS per workgroup step
     bool no_score = false;      // the caller passes no score output
     size_t part_offset = 0;     // byte offset of the partial lists (G > 1)
     size_t score_offset = 0;    // byte offset of the score rows a separate sort needs
@@ -59,6 +61,10 @@ struct Plan {
 };
 
 bool supported(int dtype, int H, int D);
+// Staged key tiles other than kKeysPerTile are built for H = 64, D = 128
+// only (bf16: 32, 128, 192, 256; fp8: 128); the default there is 128.
+bool key_tile_supported(int key_tile, int dtype, int H, int D);
+int default_key_tile(int H, int D);
 
 // Validates every argument and fills `plan`.  num_cus must be > 0.
 // no_score: the call writes no scores (also implied by CSA_FLAG_NO_SCORE).

@@ -952,7 +952,7 @@ struct Epi {
 // output row itself with one range) for the merge and sort passes.
 // Otherwise units are query blocks and each row leaves the kernel sorted
 // (next_pow2(k) <= kStageSlots).
-template <int H, int D, bool FP8, bool SPLIT>
+template <int H, int D, bool FP8, bool SPLIT, int KT = kKeysPerTile>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 stream_topk_kernel(StreamArgs a)
 {
@@ -961,14 +961,23 @@ stream_topk_kernel(StreamArgs a)
     using E = Epi<H>;
     constexpr int QW = 64 / H;                       // positions per wave (64 rows)
     constexpr int QB = kWaves * QW;                  // positions per block
-    constexpr int KT = kKeysPerTile;
+    // KT keys are staged per LDS tile (one workgroup barrier each); the
+    // waves score and filter them CT = 64 at a time (one key per lane), in
+    // two 32-key halves.  KT = 32 stages one half at a time.
+    constexpr int CT = 64;
+    static_assert(KT == 32 || KT % CT == 0, "key tile: 32 or a multiple of 64 keys");
+    static_assert(!FP8 || KT >= CT, "fp8 key scales are staged 64 at a time");
+    constexpr int NSUB = KT >= CT ? KT / CT : 1;     // compute tiles per staged tile
+    constexpr bool HALF_TILES = KT < CT;             // a staged tile is one half
     constexpr int NDS = D / O::KSTEP;                // K steps per half tile
     constexpr int ROWB = D * O::ESZ;                 // LDS key row (swizzled, unpadded)
     constexpr int NC = ROWB / 16;                    // 16-byte chunks per key row
     constexpr int TILEB = KT * ROWB;
     constexpr int NDMA = TILEB / 1024;               // 1 KB wave DMA loads per tile
     constexpr int NDMA_W = (NDMA + kWaves - 1) / kWaves;
-    constexpr int NBUF = 3;                          // LDS ring of key tiles
+    // LDS ring of staged tiles: three (two ahead) while they fit beside the
+    // staging area, else two
+    constexpr int NBUF = 3 * TILEB <= kWaves * 2 * kStageSlots * 4 ? 3 : 2;
     constexpr int PD = NBUF - 1;                     // tiles loaded ahead
     constexpr int NB = 512 / QW;                     // threshold bins per position
     constexpr int HEAD = NB / 8 > 1 ? NB / 8 : 1;    // headroom above the max seen
@@ -1073,7 +1082,7 @@ stream_topk_kernel(StreamArgs a)
         // Filter the wave's scores against key tile `it` and append the
         // survivors to the candidate logs (see the threshold histogram).
         auto consume = [&](const float (&sc)[QW], int it) {
-            const int kt = klo + it * KT;
+            const int kt = klo + it * CT;
             const int key = kt + lane;
 #pragma unroll
             for (int qi = 0; qi < QW; ++qi) {
@@ -1105,7 +1114,7 @@ stream_topk_kernel(StreamArgs a)
                 const int added = __popcll(mk);
                 cnt[qi] += added;
                 pend[qi] += added;
-                const bool full = cnt[qi] > a.log_cap - KT;
+                const bool full = cnt[qi] > a.log_cap - CT;
                 if (cnt[qi] >= a.topk && (pend[qi] >= UPD || full)) {
                     // raise tau to the lower edge of the highest bin that
                     // still has k candidates at or above it, minus one
@@ -1126,7 +1135,7 @@ stream_topk_kernel(StreamArgs a)
                 if (full) {
                     cnt[qi] = __builtin_amdgcn_readfirstlane(compact_log(lu, li, cnt[qi], tau[qi], lane));
                     const int room = a.topk + (a.log_cap - a.topk) / 2;
-                    if (cnt[qi] > (room < a.log_cap - KT ? room : a.log_cap - KT)) {
+                    if (cnt[qi] > (room < a.log_cap - CT ? room : a.log_cap - CT)) {
                         // the bins could not separate enough: exact merge
                         tau[qi] = __builtin_amdgcn_readfirstlane(merge_log(lu, li, cnt[qi], a.topk, rhist, lane));
                         cnt[qi] = a.topk;
@@ -1143,11 +1152,12 @@ stream_topk_kernel(StreamArgs a)
         // through each lane's source address.
         const unsigned char *kbase = a.k + b * a.T * (D * O::ESZ);
         const float *ksbase = FP8 ? a.k_scale + b * a.T : nullptr;
-        // DMA loads this wave issues per tile (the vmcnt it waits on)
+        // DMA loads this wave issues per tile (the vmcnt it waits on); with
+        // fp8, waves 0 .. NSUB-1 also load 64 key scales each
         const int my_dma = (NDMA > wave ? (NDMA - wave + kWaves - 1) / kWaves : 0) +
-                           ((FP8 && wave == 0) ? 1 : 0);
-        auto dma_tile = [&](int it, int buf) {
-            const int64_t row0 = int64_t(klo) + int64_t(it) * KT;
+                           ((FP8 && wave < NSUB) ? 1 : 0);
+        auto dma_tile = [&](int st, int buf) {
+            const int64_t row0 = int64_t(klo) + int64_t(st) * KT;
             const unsigned char *tb = kbase + row0 * ROWB;  // first key row of the tile
             // rows past T are never used: they repeat row T-1
             const int rmax = a.T - row0 - 1 < KT - 1 ? int(a.T - row0 - 1) : KT - 1;
@@ -1165,11 +1175,12 @@ stream_topk_kernel(StreamArgs a)
                 }
             }
             if constexpr (FP8) {
-                if (wave == 0) {
-                    int64_t key = row0 + lane;
+                if (wave < NSUB) {
+                    int64_t key = row0 + wave * CT + lane;
                     key = key < a.T ? key : a.T - 1;
                     __builtin_amdgcn_global_load_lds(
-                        ksbase + key, (__attribute__((address_space(3))) void *)&s_ks[buf][0], 4, 0, 0);
+                        ksbase + key,
+                        (__attribute__((address_space(3))) void *)&s_ks[buf][wave * CT], 4, 0, 0);
                 }
             }
         };
@@ -1192,16 +1203,17 @@ stream_topk_kernel(StreamArgs a)
             }
             __builtin_amdgcn_s_barrier();
         };
-        // loads this wave issued after those of tile t+1, once the tiles up
-        // to min(t + PD, ntiles - 1) are staged
-        auto later_loads = [&](int t, int ntiles) {
-            const int last = t + PD < ntiles - 1 ? t + PD : ntiles - 1;
+        // loads this wave issued after those of staged tile t+1, once the
+        // tiles up to min(t + PD, nst - 1) are staged
+        auto later_loads = [&](int t, int nst) {
+            const int last = t + PD < nst - 1 ? t + PD : nst - 1;
             return last > t + 1 ? my_dma * (last - t - 1) : 0;
         };
-        // the 2*NDS MFMAs of the wave's rows against 32-key half ks of tile buf
+        // the 2*NDS MFMAs of the wave's rows against the 32 keys at row r0 of
+        // staged tile buf
         f32x16_t acc[2];
-        auto mma_half = [&](int buf, int ks) {
-            const int r = ks * 32 + col;
+        auto mma_half = [&](int buf, int r0) {
+            const int r = r0 + col;
             const unsigned char *kb = &s_k[buf][r * ROWB];
 #pragma unroll
             for (int ds = 0; ds < NDS; ++ds) {
@@ -1221,7 +1233,7 @@ stream_topk_kernel(StreamArgs a)
             }
             __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         };
-        // scores of tile it from the two half partials; filter and append
+        // scores of compute tile it from the two half partials; filter and append
         auto finish = [&](const float (&ha)[E::NP], const float (&hb)[E::NP], int it, float ksv) {
             float sc[QW];
             E::combine(ha, hb, sc);
@@ -1231,56 +1243,91 @@ stream_topk_kernel(StreamArgs a)
             consume(sc, it);
         };
 
-        // Waves 0-3 run, per tile i: MFMA(half 0), its epilogue, MFMA(half 1),
-        // its epilogue, the filter.  Waves 4-7 (the second wave of each SIMD)
-        // run the same steps half a tile later: they open tile i with the
-        // epilogue and filter of tile i-1 and close it with MFMA(half 1),
-        // whose accumulators they carry over the barrier.  The two waves of a
-        // SIMD thus alternate between matrix-core and VALU work.
+        // Waves 0-3 run, per compute tile i: MFMA(half 0), its epilogue,
+        // MFMA(half 1), its epilogue, the filter.  Waves 4-7 (the second wave
+        // of each SIMD) run the same steps half a tile later: they open tile i
+        // with the epilogue and filter of tile i-1 and close it with MFMA(half
+        // 1), whose accumulators they carry over the barrier.  The two waves
+        // of a SIMD thus alternate between matrix-core and VALU work.
         const bool lagging = wave >= kWaves / 2;
-        const int ntiles = n_hi > klo ? (n_hi - klo + KT - 1) / KT : 0;
+        const int ntiles = n_hi > klo ? (n_hi - klo + CT - 1) / CT : 0;  // compute tiles
+        const int nst = n_hi > klo ? (n_hi - klo + KT - 1) / KT : 0;     // staged tiles
         // every wave is past its last read of the ring (previous block)
         __syncthreads();
-        for (int t = 0; t < PD && t < ntiles; ++t) dma_tile(t, t);
-        sync_tiles(later_loads(-1, ntiles));
+        for (int t = 0; t < PD && t < nst; ++t) dma_tile(t, t);
+        sync_tiles(later_loads(-1, nst));
         float ksv_prev = 1.f;
         float h0[E::NP], h1[E::NP];
 #pragma unroll 1
         for (int it = 0; it < ntiles; ++it) {
-            const int buf = it % NBUF;
+            // staged tile and row of half 0 (half 1: the next 32 rows, or with
+            // half-tile staging row 0 of the next staged tile)
+            const int st = HALF_TILES ? 2 * it : it / NSUB;
+            const int buf = st % NBUF;
+            const int r0 = HALF_TILES ? 0 : (it % NSUB) * CT;
             float ksv = 1.f;
-            if constexpr (FP8) ksv = s_ks[buf][lane];
-            // Each wave stages its share of tile it+PD (over tile it-1, which
+            if constexpr (FP8) ksv = s_ks[buf][r0 + lane];
+            // Each wave stages its share of tile st+PD (over tile st-1, which
             // every wave has finished) after its own filter step, so that the
             // leading and the lagging waves issue their loads half a tile
             // apart.
-            const bool stage = it + PD < ntiles;
+            const bool stage = (HALF_TILES || it % NSUB == 0) && st + PD < nst;
+            const bool last = HALF_TILES || it % NSUB == NSUB - 1 || it == ntiles - 1;
             // The epilogue of one half tile is issued before the next half's
             // MFMAs (a scheduling barrier), so both halves share one set of
             // accumulator registers: the other wave of the SIMD keeps the
             // matrix core busy meanwhile.
-            if (!lagging) {
-                mma_half(buf, 0);
-                E::partial(acc, wr, h0);
-                __builtin_amdgcn_sched_barrier(0);
-                mma_half(buf, 1);
-                E::partial(acc, wr, h1);
-                finish(h0, h1, it, ksv);
-                if (stage) dma_tile(it + PD, (it + PD) % NBUF);
-            } else {
-                if (it > 0) {
+            if constexpr (HALF_TILES) {
+                const int buf1 = (st + 1) % NBUF;
+                const bool stage1 = st + 1 + PD < nst;
+                if (!lagging) {
+                    mma_half(buf, 0);
+                    E::partial(acc, wr, h0);
+                    if (stage) dma_tile(st + PD, (st + PD) % NBUF);
+                    sync_tiles(later_loads(st, nst));
+                    mma_half(buf1, 0);
                     E::partial(acc, wr, h1);
-                    __builtin_amdgcn_sched_barrier(0);
-                    finish(h0, h1, it - 1, ksv_prev);
+                    finish(h0, h1, it, ksv);
+                    if (stage1) dma_tile(st + 1 + PD, (st + 1 + PD) % NBUF);
+                } else {
+                    if (it > 0) {
+                        E::partial(acc, wr, h1);
+                        __builtin_amdgcn_sched_barrier(0);
+                        finish(h0, h1, it - 1, ksv_prev);
+                    }
+                    if (stage) dma_tile(st + PD, (st + PD) % NBUF);
+                    mma_half(buf, 0);
+                    E::partial(acc, wr, h0);
+                    sync_tiles(later_loads(st, nst));
+                    if (stage1) dma_tile(st + 1 + PD, (st + 1 + PD) % NBUF);
+                    mma_half(buf1, 0);
                 }
-                if (stage) dma_tile(it + PD, (it + PD) % NBUF);
-                mma_half(buf, 0);
-                E::partial(acc, wr, h0);
-                __builtin_amdgcn_sched_barrier(0);
-                mma_half(buf, 1);
+                ksv_prev = ksv;
+                sync_tiles(later_loads(st + 1, nst));
+            } else {
+                if (!lagging) {
+                    mma_half(buf, r0);
+                    E::partial(acc, wr, h0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    mma_half(buf, r0 + 32);
+                    E::partial(acc, wr, h1);
+                    finish(h0, h1, it, ksv);
+                    if (stage) dma_tile(st + PD, (st + PD) % NBUF);
+                } else {
+                    if (it > 0) {
+                        E::partial(acc, wr, h1);
+                        __builtin_amdgcn_sched_barrier(0);
+                        finish(h0, h1, it - 1, ksv_prev);
+                    }
+                    if (stage) dma_tile(st + PD, (st + PD) % NBUF);
+                    mma_half(buf, r0);
+                    E::partial(acc, wr, h0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    mma_half(buf, r0 + 32);
+                }
+                ksv_prev = ksv;
+                if (last) sync_tiles(later_loads(st, nst));
             }
-            ksv_prev = ksv;
-            sync_tiles(later_loads(it, ntiles));
         }
         if (lagging && ntiles > 0) {
             E::partial(acc, wr, h1);
@@ -1333,12 +1380,43 @@ stream_topk_kernel(StreamArgs a)
 template <int H, int D, bool FP8>
 static hipError_t launch_one(const StreamArgs &a, int grid, hipStream_t s)
 {
-    if (a.sort_e == 0)
+    if (a.sort_e == 0) {
         hipLaunchKernelGGL((stream_topk_kernel<H, D, FP8, true>), dim3(grid), dim3(kThreads), 0,
                            s, a);
-    else
-        hipLaunchKernelGGL((stream_topk_kernel<H, D, FP8, false>), dim3(grid), dim3(kThreads), 0,
-                           s, a);
+        return hipGetLastError();
+    }
+    if constexpr (H == 64 && D == 128 && FP8) {
+        if (a.key_tile == 128) {
+            hipLaunchKernelGGL((stream_topk_kernel<H, D, FP8, false, 128>), dim3(grid),
+                               dim3(kThreads), 0, s, a);
+            return hipGetLastError();
+        }
+    }
+    if constexpr (H == 64 && D == 128 && !FP8) {
+        // the other staged key tiles (a speed knob) of this one shape
+        switch (a.key_tile) {
+        case 32:
+            hipLaunchKernelGGL((stream_topk_kernel<H, D, FP8, false, 32>), dim3(grid),
+                               dim3(kThreads), 0, s, a);
+            return hipGetLastError();
+        case 128:
+            hipLaunchKernelGGL((stream_topk_kernel<H, D, FP8, false, 128>), dim3(grid),
+                               dim3(kThreads), 0, s, a);
+            return hipGetLastError();
+        case 192:
+            hipLaunchKernelGGL((stream_topk_kernel<H, D, FP8, false, 192>), dim3(grid),
+                               dim3(kThreads), 0, s, a);
+            return hipGetLastError();
+        case 256:
+            hipLaunchKernelGGL((stream_topk_kernel<H, D, FP8, false, 256>), dim3(grid),
+                               dim3(kThreads), 0, s, a);
+            return hipGetLastError();
+        default: break;
+        }
+    }
+    if (a.key_tile != kKeysPerTile) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((stream_topk_kernel<H, D, FP8, false>), dim3(grid), dim3(kThreads), 0, s,
+                       a);
     return hipGetLastError();
 }
 

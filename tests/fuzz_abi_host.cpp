@@ -100,6 +100,9 @@ int main(int argc, char **argv)
         o.row_offset = pick64();
         o.key_splits = (rng() % 3 == 0) ? pick32() : 0;
         o.flags = int32_t(rng() % 16 == 0 ? 2 : rng() % 4 == 0 ? CSA_FLAG_NO_SCORE : 0);
+        const int32_t tiles[] = {0, 0, 0, 64, 32, 128, 192, 256, 96, -64};
+        o.key_tile = tiles[rng() % 10];
+        o.reserved2 = (rng() % 32 == 0) ? 1 : 0;
         o.workspace = (rng() & 1) ? p : nullptr;
         o.workspace_bytes = size_t(rng() % (size_t(1) << 34));
         const int32_t m = pick32(), k = pick32();

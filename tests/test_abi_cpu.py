@@ -174,10 +174,16 @@ def test_key_splits_plan(lib):
     few = csa.plan_query(csa.make_desc(1, 8, 100, 64, 128), 4, 16, opts(row_offset=1000,
                                                                         key_splits=50))
     assert few.key_splits == 2                         # 100 keys -> 2 tiles
-    # the partial lists stay under 1 GiB: G is lowered
-    wide = csa.plan_query(csa.make_desc(1, 2048, 65536, 64, 128), 4, 16384,
+    # automatic ranges keep the partial lists under 1 GiB, requested ones
+    # under 64 GiB: G is lowered
+    auto = csa.plan_query(csa.make_desc(1, 64, 65536, 64, 128), 4, 16384, opts(row_offset=262080))
+    assert 64 * auto.key_splits * 16384 * 8 <= 1 << 30
+    wide = csa.plan_query(csa.make_desc(1, 65536, 65536, 64, 128), 4, 16384,
                           opts(row_offset=262144, key_splits=64))
-    assert 2048 * wide.key_splits * 16384 * 8 <= 1 << 30
+    assert 65536 * wide.key_splits * 16384 * 8 <= 1 << 36 and wide.key_splits == 8
+    # the key-range sweep of the S=65,536 workload: 16 ranges of 1,024 keys
+    sweep = csa.plan_query(csa.make_desc(1, 65536, 16384, 64, 128), 4, 2048, opts(key_splits=16))
+    assert sweep.key_splits == 16
 
 
 def test_key_splits_validation(lib):
@@ -399,3 +405,27 @@ def test_static_entry_point_validation(lib):
                                 ctypes.byref(opts()), None) == B.CSA_ERR_WORKSPACE
     assert lib.csa_index_static(16, 16, 16, ctypes.byref(d), 0, 8, 16, 16,
                                 ctypes.byref(opts()), None) == B.CSA_ERR_INVALID_ARG
+
+
+def test_key_tile_option(lib):
+    """Staged key tiles other than 64 exist for bf16, H = 64, D = 128 rows
+    sorted by the scoring kernel; elsewhere they are unsupported."""
+    d = csa.make_desc(1, 65536, 16384, 64, 128)
+    for kt in (32, 64, 128, 192, 256):
+        assert csa.plan_query(d, 4, 2048, opts(key_tile=kt)).keys_per_tile == kt
+    assert csa.plan_query(d, 4, 2048, opts()).keys_per_tile == 128   # default for this shape
+    assert csa.plan_query(d, 4, 4096, opts()).keys_per_tile == 64    # rows sorted separately
+    assert csa.plan_query(csa.make_desc(1, 100, 25, 32, 128), 4, 8, opts()).keys_per_tile == 64
+    f8 = csa.make_desc(1, 65536, 16384, 64, 128, B.CSA_FP8_E4M3FN, 16, 16)
+    assert csa.plan_query(f8, 4, 2048, opts()).keys_per_tile == 128
+    assert csa.plan_query(f8, 4, 2048, opts(key_tile=64)).keys_per_tile == 64
+    assert bad(lib, f8, k=2048, opt=opts(key_tile=256)) == B.CSA_ERR_UNSUPPORTED
+    assert bad(lib, d, k=2048, opt=opts(key_tile=96)) == B.CSA_ERR_UNSUPPORTED
+    assert bad(lib, d, k=4096, opt=opts(key_tile=128)) == B.CSA_ERR_UNSUPPORTED  # separate sort
+    assert bad(lib, d, k=2048, opt=opts(key_tile=128, key_splits=4)) == B.CSA_ERR_UNSUPPORTED
+    assert bad(lib, csa.make_desc(1, 100, 25, 32, 128), opt=opts(key_tile=128)) == \
+        B.CSA_ERR_UNSUPPORTED
+    assert bad(lib, d, opt=opts(key_tile=-64)) == B.CSA_ERR_INVALID_ARG
+    o = opts()
+    o.reserved2 = 1
+    assert bad(lib, d, opt=o) == B.CSA_ERR_INVALID_ARG

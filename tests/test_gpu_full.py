@@ -10,7 +10,8 @@ import numpy as np
 import pytest
 import torch
 
-from csa_synth import CHUNK_SWEEP, TOPK_SWEEP, WORKLOADS, Workload, make_inputs, sample_rows
+from csa_synth import (CHUNK_SWEEP, KEY_TILE_SWEEP, RANGE_SWEEP, TOPK_SWEEP, WORKLOADS, Workload,
+                       make_inputs, sample_rows)
 from checker import OracleView, compare_exact, compare_tolerant
 
 pytestmark = pytest.mark.gpu
@@ -59,6 +60,34 @@ def test_s64k_chunk_sweep_bit_identical_and_sampled(csa):
     rows = sample_rows(wl.S, wl.m, wl.k, n=256, chunk=CHUNK_SWEEP[0])
     stats = _sample_check(inp, wl, ref_idx, ref_score, rows, exact=False)
     print(f"[sweep] chunks {CHUNK_SWEEP} k={wl.k} {stats}", flush=True)
+    assert stats["recall"] > 0.999
+
+
+def test_s64k_key_tile_and_range_sweeps_bit_identical(csa):
+    """The staged key-tile sweep (32 ... 256 keys) and the key-range sweep
+    (ranges of 1,024 ... 16,384 keys, each range's exact top-k merged) of
+    the S=65,536 workload: every cell bit-identical to the default call,
+    which matches the oracle on 256 sampled rows."""
+    wl = WORKLOADS["s64k"]
+    print(f"\n[case] {wl} key tiles {KEY_TILE_SWEEP} ranges {RANGE_SWEEP}", flush=True)
+    inp = make_inputs(wl, seed=0, device="cuda")
+    ref_idx, ref_score = _run(csa, inp, wl)
+    for kt in KEY_TILE_SWEEP:
+        print(f"[case] key_tile {kt}", flush=True)
+        idx, score = _run(csa, inp, wl, key_tile=kt)
+        assert torch.equal(idx, ref_idx), f"indices differ at key tile {kt}"
+        assert torch.equal(score, ref_score), f"scores differ at key tile {kt}"
+        del idx, score
+    for r in RANGE_SWEEP:
+        G = wl.n_keys // r
+        print(f"[case] {G} key ranges of {r} keys", flush=True)
+        idx, score = _run(csa, inp, wl, key_splits=G)
+        assert torch.equal(idx, ref_idx), f"indices differ with ranges of {r} keys"
+        assert torch.equal(score, ref_score), f"scores differ with ranges of {r} keys"
+        del idx, score
+    rows = sample_rows(wl.S, wl.m, wl.k, n=256)
+    stats = _sample_check(inp, wl, ref_idx, ref_score, rows, exact=False)
+    print(f"[sweep] key tiles and ranges k={wl.k} {stats}", flush=True)
     assert stats["recall"] > 0.999
 
 

@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 import torch
 
-from csa_synth import CHUNK_SWEEP, WORKLOADS, Workload, make_inputs, sample_rows
+from csa_synth import CHUNK_SWEEP, KEY_TILE_SWEEP, WORKLOADS, Workload, make_inputs, sample_rows
 from checker import OracleView, compare_exact, compare_tolerant
 
 pytestmark = pytest.mark.gpu
@@ -22,18 +22,18 @@ def csa():
     return lib
 
 
-def _run(csa, inp, wl, chunk=0, row_offset=0):
+def _run(csa, inp, wl, chunk=0, row_offset=0, key_tile=0):
     out_idx, out_score = csa.index(inp["q"], inp["w"], inp["k"], wl.m, wl.k,
                                    q_scale=inp.get("q_scale"), k_scale=inp.get("k_scale"),
-                                   chunk_keys=chunk, row_offset=row_offset)
+                                   chunk_keys=chunk, row_offset=row_offset, key_tile=key_tile)
     torch.cuda.synchronize()
     return out_idx, out_score
 
 
-def _check(csa, wl, seed=0, rows=None, chunk=0, exact=None, b_list=None):
-    print(f"\n[case] {wl} seed={seed} chunk={chunk}", flush=True)
+def _check(csa, wl, seed=0, rows=None, chunk=0, exact=None, b_list=None, key_tile=0):
+    print(f"\n[case] {wl} seed={seed} chunk={chunk} key_tile={key_tile}", flush=True)
     inp = make_inputs(wl, seed=seed, device="cuda")
-    out_idx, out_score = _run(csa, inp, wl, chunk=chunk)
+    out_idx, out_score = _run(csa, inp, wl, chunk=chunk, key_tile=key_tile)
     exact = (wl.dist == "int") if exact is None else exact
     stats = []
     for b in (b_list if b_list is not None else range(wl.B)):
@@ -77,6 +77,17 @@ SMALL_EXACT = [
 def test_small_integer_exact(csa, shape):
     B, S, m, H, D, k, T = shape
     _check(csa, Workload("small", B=B, S=S, m=m, H=H, D=D, k=k, dist="int", T=T), seed=S)
+
+
+@pytest.mark.parametrize("key_tile", KEY_TILE_SWEEP)
+@pytest.mark.parametrize("shape", [(1, 3001, 4, 100, 750), (2, 999, 3, 2048, -1),
+                                   (1, 1203, 1, 37, 1203)], ids=lambda s: "B%dS%dm%dk%dT%d" % s)
+def test_key_tiles_integer_exact(csa, shape, key_tile):
+    """Every staged key-tile size, on integer inputs whose key counts are no
+    multiple of any tile (ragged last tiles), every row exact."""
+    B, S, m, k, T = shape
+    _check(csa, Workload("tiles", B=B, S=S, m=m, H=64, D=128, k=k, dist="int", T=T), seed=S + k,
+           key_tile=key_tile)
 
 
 @pytest.mark.parametrize("chunk", [64, 192, 1024])
