@@ -103,11 +103,34 @@ def cpu_baseline(inp, wl, nrows, seed=0):
     oracle.topk_rows(q, w, k, pos, wl.m, wl.k, dtype=wl.dtype, q_scale_rows=qs, k_scale=ks,
                      nthreads=threads)
     dt = time.perf_counter() - t0
+    # one thread on every (len/16)-th row of the same sample
+    sub = np.arange(0, len(rows), max(1, len(rows) // 16))[:16]
+    n1 = len(sub)
+    t1 = time.perf_counter()
+    oracle.topk_rows(q[sub], w[sub], k, pos[sub], wl.m, wl.k, dtype=wl.dtype,
+                     q_scale_rows=qs[sub] if qs is not None else None, k_scale=ks, nthreads=1)
+    dt1 = time.perf_counter() - t1
     n_vis = np.minimum(wl.n_keys, (pos + 1) // wl.m)
     return {"value": len(rows) / dt, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "single_thread_value": n1 / dt1,
             "sample": (f"{len(rows)} seeded uniform rows of {wl.name} (mean visible keys "
                        f"{float(n_vis.mean()):.0f}; workload mean {wl.n_keys / 2:.0f}), "
-                       f"fp64 scores + full sort, {dt:.1f} s")}
+                       f"fp64 scores + full sort, {dt:.1f} s on {threads} threads; "
+                       f"single_thread_value from {n1} of them spread over the sample, on "
+                       f"one thread (mean visible keys {float(n_vis[sub].mean()):.0f}), "
+                       f"{dt1:.1f} s")}
+
+
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None if unavailable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 ATTN_METRIC = "sparse attention over the selected keys, queries/sec, 1 GPU"
@@ -305,6 +328,10 @@ def main():
     ap.add_argument("--key-splits", type=int, default=0,
                     help="key ranges per query block (0 = automatic, 1 = none)")
     ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--no-score", action="store_true",
+                    help="call without a score output (out_score = NULL): indices only")
+    ap.add_argument("--key-tile", type=int, default=0,
+                    help="keys staged per LDS tile (0 = the library's default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="time the five-point sweeps of the S=65,536 workload (chunk size, "
@@ -356,27 +383,35 @@ def main():
     wl = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    torch.cuda.synchronize()
+    free0, total = torch.cuda.mem_get_info(dev)       # hipMemGetInfo
     torch.cuda.reset_peak_memory_stats(dev)
     inp = make_inputs(wl, seed=0, device=dev)
     out_idx = torch.empty((wl.B, wl.S, wl.k), dtype=torch.int32, device=dev)
-    out_score = torch.empty((wl.B, wl.S, wl.k), dtype=torch.float32, device=dev)
+    want_score = not args.no_score
+    out_score = (torch.empty((wl.B, wl.S, wl.k), dtype=torch.float32, device=dev)
+                 if want_score else None)
     ws = csa.workspace_for(inp["q"], inp["k"], wl.m, wl.k, args.chunk, wl.row_offset,
-                           args.key_splits)
+                           args.key_splits, want_score=want_score)
     torch.cuda.synchronize()
     in_bytes = sum(t.numel() * t.element_size() for t in inp.values())
-    out_bytes = out_idx.numel() * 4 + out_score.numel() * 4
+    out_bytes = out_idx.numel() * 4 + (out_score.numel() * 4 if want_score else 0)
     ws_bytes = ws.numel()
     events = csa.HipEvents(args.steps)
     stream = torch.cuda.current_stream(dev)
-    plan = csa.plan_query(csa.make_desc(wl.B, wl.S, wl.n_keys, wl.H, wl.D), wl.m, wl.k,
+    plan = csa.plan_query(csa.make_desc(wl.B, wl.S, wl.n_keys, wl.H, wl.D, csa.CSA_FP8_E4M3FN
+                                        if wl.dtype == "e4m3fn" else csa.CSA_BF16,
+                                        1 if wl.dtype == "e4m3fn" else 0,
+                                        1 if wl.dtype == "e4m3fn" else 0), wl.m, wl.k,
                           csa.make_options(args.chunk, wl.row_offset,
-                                           key_splits=args.key_splits))
+                                           key_splits=args.key_splits, key_tile=args.key_tile))
 
     def step(timing=None):
         csa.index(inp["q"], inp["w"], inp["k"], wl.m, wl.k, q_scale=inp.get("q_scale"),
                   k_scale=inp.get("k_scale"), out_idx=out_idx, out_score=out_score,
                   chunk_keys=args.chunk, row_offset=wl.row_offset, key_splits=args.key_splits,
-                  workspace=ws, timing=timing, stream=stream)
+                  workspace=ws, timing=timing, stream=stream, want_score=want_score,
+                  key_tile=args.key_tile)
 
     for _ in range(args.warmup):
         step()
@@ -389,6 +424,8 @@ def main():
     kernel_ms = [events.elapsed_ms(i) for i in range(args.steps)]
     events.close()
     peak_hbm = torch.cuda.max_memory_allocated(dev)
+    free1, _ = torch.cuda.mem_get_info(dev)
+    device_used = free0 - free1   # what the device lost since the start, torch's cache included
 
     pairs = visible_pairs(wl.S, wl.n_keys, wl.m, wl.B, wl.row_offset)
     flops = 2.0 * wl.H * wl.D * pairs
@@ -419,12 +456,14 @@ def main():
         "config": {"workload": wl.name, "B": wl.B, "S": wl.S, "T": wl.n_keys, "H_I": wl.H,
                    "d_I": wl.D, "m": wl.m, "k": wl.k, "dist": wl.dist,
                    "row_offset": wl.row_offset, "chunk_keys": args.chunk or None,
-                   "key_splits": plan.key_splits},
+                   "key_splits": plan.key_splits, "key_tile": plan.keys_per_tile},
         "tflops": step_tflops,
         "mfma_pct_peak": 100.0 * step_tflops / peak,
         "peak_hbm_gb": peak_hbm / 1e9,
         "hbm_breakdown_gb": {"inputs": in_bytes / 1e9, "outputs": out_bytes / 1e9,
                              "workspace": ws_bytes / 1e9},
+        "hbm_device_used_gb": device_used / 1e9,
+        "scores_returned": want_score,
         "scoring_kernel_ms": kernel_avg,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic_from_profile(wl.name)},

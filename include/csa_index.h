@@ -35,6 +35,8 @@
  *     exception crosses this boundary.
  *   - Results are deterministic: bitwise identical across runs, chunk sizes,
  *     key splits and launch shapes (no floating-point atomics).
+ *   - Diagnostics: with the environment variable CSA_LOG set (not "0"),
+ *     every csa_index / csa_index_ex call prints its launch plan to stderr.
  */
 #ifndef CSA_INDEX_H
 #define CSA_INDEX_H
@@ -150,6 +152,8 @@ typedef struct {
     int32_t key_splits;          /* key ranges per query block (G >= 1)     */
     int64_t n_blocks;            /* query blocks over all batch entries     */
     size_t workspace_bytes;      /* device scratch needed                   */
+    int32_t keys_per_range;      /* keys of each range (G > 1), else 0      */
+    int32_t reserved;            /* 0                                       */
 } csa_plan_info;
 
 /*

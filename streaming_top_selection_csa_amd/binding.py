@@ -53,7 +53,8 @@ class CsaPlanInfo(ctypes.Structure):
     _fields_ = [("queries_per_block", ctypes.c_int32), ("keys_per_tile", ctypes.c_int32),
                 ("chunk_keys", ctypes.c_int32), ("log_capacity", ctypes.c_int32),
                 ("grid", ctypes.c_int32), ("key_splits", ctypes.c_int32),
-                ("n_blocks", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t)]
+                ("n_blocks", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
+                ("keys_per_range", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class CsaAttnDesc(ctypes.Structure):

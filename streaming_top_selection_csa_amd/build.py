@@ -26,8 +26,8 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     # packed fp32 vector ops stay off (the host pass ignores this feature)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA results in VGPRs (the epilogue reads every accumulator with the
-    # VALU); q operands stay in AGPRs
+    # MFMA results in VGPRs: the epilogue reads every accumulator with the
+    # VALU (at two waves per SIMD a wave's 256 registers are all VGPRs)
     "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", INCLUDE, "-I", CSRC,
 ]

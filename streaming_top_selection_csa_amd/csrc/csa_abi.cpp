@@ -9,6 +9,8 @@
 #include <hip/hip_runtime_api.h>
 
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
 
 #include "csa_index.h"
 #include "csa_kernels.hpp"
@@ -46,6 +48,31 @@ int plan_for(const csa_desc *desc, int32_t m, int32_t k, const csa_options *opt,
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// CSA_LOG set to anything but "" or "0": each call prints its plan to stderr.
+bool log_plans()
+{
+    static const bool on = [] {
+        const char *e = std::getenv("CSA_LOG");
+        return e && *e && !(e[0] == '0' && e[1] == 0);
+    }();
+    return on;
+}
+
+void print_plan(const csa::Plan &p, int cus, bool caller_ws)
+{
+    std::fprintf(stderr,
+                 "csa_index: B=%lld S=%lld T=%lld H=%d D=%d %s m=%d k=%d row_offset=%lld | "
+                 "grid=%d of %d CUs, %lld blocks of %d positions, key tile %d, chunk %d "
+                 "(log %d), key ranges %d of %d keys, rows sorted %s, scores %s, "
+                 "workspace %zu bytes (%s)\n",
+                 (long long)p.B, (long long)p.S, (long long)p.T, p.H, p.D, p.fp8 ? "fp8" : "bf16",
+                 p.m, p.k, (long long)p.row_offset, p.grid, cus, (long long)p.n_blocks, p.QB,
+                 p.key_tile, p.chunk, p.log_cap, p.n_splits, p.split_keys,
+                 p.sort_e > 0 ? "in the scoring kernel" : "by a separate pass",
+                 p.no_score ? "not returned" : "returned", p.ws_bytes,
+                 caller_ws ? "caller" : "stream-ordered allocation");
+}
+
 }  // namespace
 
 extern "C" const char *csa_status_string(int status)
@@ -76,6 +103,8 @@ extern "C" int csa_plan_query(const csa_desc *desc, int32_t m, int32_t k,
     out->key_splits = p.n_splits;
     out->n_blocks = p.n_blocks;
     out->workspace_bytes = p.ws_bytes;
+    out->keys_per_range = p.n_splits > 1 ? p.split_keys : 0;
+    out->reserved = 0;
     return CSA_OK;
 }
 
@@ -111,7 +140,9 @@ extern "C" int csa_index_ex(const void *q, const float *w, const void *k_cmp,
         if (opt->workspace_bytes < p.ws_bytes || !aligned(opt->workspace, 256))
             return CSA_ERR_WORKSPACE;
         ws = opt->workspace;
-    } else if (p.ws_bytes > 0) {
+    }
+    if (log_plans()) print_plan(p, cus, ws != nullptr);
+    if (!ws && p.ws_bytes > 0) {
         if (hipMallocAsync(&ws, p.ws_bytes, stream) != hipSuccess) return CSA_ERR_HIP;
         owned = true;
     }

@@ -429,3 +429,66 @@ def test_key_tile_option(lib):
     o = opts()
     o.reserved2 = 1
     assert bad(lib, d, opt=o) == B.CSA_ERR_INVALID_ARG
+
+
+def _unit_coverage(desc, m, k, opt):
+    """Walks the scoring kernel's work decomposition for a plan: the
+    persistent grid's dealing of units (XCD-grouped, snake order) and each
+    unit's (query block, key range); checks that every unit is dealt once
+    and every causally visible (b, t, s) pair is scored exactly once."""
+    import numpy as np
+    info = csa.plan_query(desc, m, k, opt)
+    B, S, T, off = desc.B, desc.S, desc.T, opt.row_offset
+    QB, G, grid = info.queries_per_block, info.key_splits, info.grid
+    R = info.keys_per_range if G > 1 else 1 << 30
+    bpb = -(-S // QB)
+    n_units = bpb * B * G
+    assert info.n_blocks == bpb * B
+    dealt = np.zeros(n_units, np.int64)
+    per_xcd = grid >> 3
+    for g in range(grid):
+        xcd, in_xcd = g & 7, g >> 3
+        rnd = 0
+        while True:
+            if grid & 7:
+                j = rnd * grid + ((grid - 1 - g) if rnd & 1 else g)
+            else:
+                j = (rnd * 8 + ((7 - xcd) if rnd & 1 else xcd)) * per_xcd + in_xcd
+            if j >= n_units:
+                break
+            dealt[j] += 1
+            rnd += 1
+    assert (dealt == 1).all()
+    nvis = lambda t: np.minimum(T, (t + 1) // m)
+    covered = np.zeros((B, S), np.int64)
+    ends = np.zeros((B, S), np.int64)       # next key each position expects
+    for j in range(n_units):
+        jq, js = j // G, j % G
+        b, blk = jq % B, bpb - 1 - jq // B
+        p0 = blk * QB
+        pos = np.arange(p0, min(p0 + QB, S))
+        klo = js * R
+        hi = min(int(nvis(off + pos[-1])), klo + R)
+        lo_t = np.full(pos.shape, klo)
+        hi_t = np.minimum(nvis(off + pos), hi)
+        n = np.maximum(hi_t - lo_t, 0)
+        # ranges of one position come in ascending, contiguous order
+        assert ((n == 0) | (lo_t == ends[b, pos])).all()
+        ends[b, pos] = np.where(n > 0, hi_t, ends[b, pos])
+        covered[b, pos] += n
+    want = nvis(off + np.arange(S))
+    assert (covered == want[None, :]).all()
+
+
+@pytest.mark.parametrize("B,S,T,m,k,off,splits", [
+    (1, 262144, 65536, 4, 2048, 0, 0),          # the headline shape, no ranges
+    (1, 64, 65536, 4, 2048, 262080, 0),         # decode: automatic ranges
+    (32, 4, 16384, 4, 2048, 65532, 0),          # 32 sequences of 4 positions
+    (2, 3001, 500, 3, 100, 7, 0),               # ragged blocks, T < S/m
+    (1, 64, 65536, 4, 2048, 262080, 7),         # requested ranges
+    (1, 5000, 1250, 4, 64, 0, 3),
+    (3, 777, 100, 1, 16, 0, 0),                 # m = 1
+])
+def test_planner_covers_every_visible_pair_once(lib, B, S, T, m, k, off, splits):
+    _unit_coverage(csa.make_desc(B, S, T, 64, 128), m, k,
+                   opts(row_offset=off, key_splits=splits))
