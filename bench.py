@@ -318,6 +318,74 @@ def sweep(csa, args):
         del out_idx, out_score, ws
 
 
+def grouped(csa, args):
+    """The grouped (approximate) indexer on the S=65,536 workload: for each
+    group size and candidate count, the time of one call and the set recall
+    of its rows against the exact path (every row, csa_index) and against
+    the CPU oracle (256 sampled rows).  One JSON line per cell."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from csa_synth import WORKLOADS, make_inputs, sample_rows, storage_numpy
+
+    wl = WORKLOADS["s64k"]
+    dev = torch.device("cuda:0")
+    inp = make_inputs(wl, seed=0, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ex_idx, _ = csa.index(inp["q"], inp["w"], inp["k"], wl.m, wl.k)
+    rows = sample_rows(wl.S, wl.m, wl.k, n=256)
+    o_idx, _ = oracle.topk_rows(storage_numpy(inp["q"][0].index_select(
+        0, torch.as_tensor(rows, device=dev))), inp["w"][0].index_select(
+        0, torch.as_tensor(rows, device=dev)).cpu().numpy(), storage_numpy(inp["k"][0]), rows,
+        wl.m, wl.k)
+
+    def recall(got, want):
+        g_valid = got >= 0
+        w_valid = want >= 0
+        inter = np.array([len(np.intersect1d(a[ga], b[wb], assume_unique=True))
+                          for a, ga, b, wb in zip(got, g_valid, want, w_valid)])
+        n = w_valid.sum(1)
+        r = np.where(n > 0, inter / np.maximum(n, 1), 1.0)
+        return float(r.mean()), float(r.min())
+
+    flops_exact = 2.0 * wl.H * wl.D * visible_pairs(wl.S, wl.n_keys, wl.m)
+    ex_np = ex_idx[0].cpu().numpy()
+    for g in (8, 16, 32, 64):
+        for C in (2048, 4096, 8192):
+            out_idx = torch.empty_like(ex_idx)
+            ws = csa.grouped_workspace_for(inp["q"], inp["k"], wl.m, wl.k, g, C, want_score=False)
+            events = csa.HipEvents(args.steps)
+
+            def step(timing=None):
+                csa.index_grouped(inp["q"], inp["w"], inp["k"], wl.m, wl.k, g, C,
+                                  out_idx=out_idx, want_score=False, workspace=ws, timing=timing,
+                                  stream=stream)
+
+            for _ in range(args.warmup):
+                step()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(args.steps):
+                step(events.pairs[i])
+            torch.cuda.synchronize()
+            ms = 1e3 * (time.perf_counter() - t0) / args.steps
+            call_ms = sum(events.elapsed_ms(i) for i in range(args.steps)) / args.steps
+            events.close()
+            got = out_idx[0].cpu().numpy()
+            r_all = recall(got, ex_np)
+            r_or = recall(got[rows], o_idx)
+            print(json.dumps({
+                "grouped": True, "workload": wl.name, "S": wl.S, "T": wl.n_keys, "k": wl.k,
+                "group": g, "candidates": C, "ms_per_step": ms, "call_ms": call_ms,
+                "queries_per_s": wl.S / (call_ms * 1e-3),
+                "exact_equivalent_tflops": flops_exact / (call_ms * 1e-3) / 1e12,
+                "recall_vs_exact_all_rows": {"mean": r_all[0], "min": r_all[1]},
+                "recall_vs_oracle_256_rows": {"mean": r_or[0], "min": r_or[1]},
+                "workspace_gb": ws.numel() / 1e9}), flush=True)
+            del ws, out_idx
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -337,6 +405,9 @@ def main():
                     help="time the five-point sweeps of the S=65,536 workload (chunk size, "
                          "top-k, staged key tile, key-range size), one JSON line per cell; "
                          "the GPU tests check every cell against the oracle")
+    ap.add_argument("--grouped", action="store_true",
+                    help="the grouped (approximate) indexer on the S=65,536 workload: time and "
+                         "set recall for group sizes 8..64 and 2,048..8,192 candidates")
     ap.add_argument("--sweep-axes", default="",
                     help="with --sweep: comma-separated subset of chunk_keys,topk,key_tile,"
                          "range_keys")
@@ -376,6 +447,9 @@ def main():
     csa.load_library()
     if args.sweep:
         sweep(csa, args)
+        return
+    if args.grouped:
+        grouped(csa, args)
         return
     if args.workload.startswith("attn-"):
         attention(csa, args)

@@ -222,6 +222,54 @@ int csa_plan_query(const csa_desc *desc, int32_t m, int32_t k,
 const char *csa_status_string(int status);
 
 /* ------------------------------------------------------------------------
+ * Grouped indexer (approximate).
+ *
+ * The query-group shared scan of the PIVOT news item (themodelwire, "PIVOT
+ * reduces sparse attention indexing bottleneck"): nearby query positions
+ * share one scan of the keys they all see, and each then refines the shared
+ * result.  The item gives no formula; this entry point computes, for every
+ * group of g consecutive positions t0 .. t0+g-1 (q rows grouped from row 0;
+ * the last group may be shorter):
+ *   1. the pooled query: per head j, bf16(mean_t q[t,j,:]) (fp32 sum over the
+ *      members in order, divided by their count, rounded to nearest even)
+ *      and the fp32 mean of w[t,j];
+ *   2. its indexer scores over the keys the first member sees,
+ *      s < n_vis(t0), and the C best of them (csa_index's order and ties);
+ *   3. for every member t: the exact score I(t, s) of each of those C keys
+ *      and of every key n_vis(t0) <= s < n_vis(t), and the top-k of them
+ *      exactly as csa_index orders and pads them.
+ * A member's result equals csa_index's whenever its true top-k keys are
+ * among those candidates; otherwise it is an approximation (its set recall
+ * below 1).  csa_index itself is never affected.
+ * ------------------------------------------------------------------------ */
+
+typedef struct {
+    int32_t group;         /* g: positions per group, a multiple of 8       */
+    int32_t candidates;    /* C: keys the shared scan keeps, k <= C <= 8192;
+                              0 = min(2k, 8192)                             */
+    int32_t reserved[2];   /* must be 0                                     */
+} csa_group_options;
+
+/*
+ * csa_index_grouped: csa_index's outputs (same shapes, order and padding;
+ * out_score may be NULL) from the grouped computation above.  Built for
+ * bf16 q and k_cmp with H = 64, D = 128 and next_pow2(k) <= 2048; other
+ * shapes return CSA_ERR_UNSUPPORTED.  opt: row_offset, chunk_keys, num_cus,
+ * workspace (csa_grouped_workspace_bytes bytes), timing (recorded around the
+ * whole sequence) as for csa_index_ex; key_splits must be 0 or 1 and
+ * key_tile 0 or 128.  Deterministic for a given g and C.
+ */
+int csa_index_grouped(const void *q, const float *w, const void *k_cmp,
+                      const csa_desc *desc, int32_t m, int32_t k,
+                      const csa_group_options *gopt, int32_t *out_idx, float *out_score,
+                      const csa_options *opt, hipStream_t stream);
+
+/* Device scratch bytes csa_index_grouped needs (0 on invalid arguments);
+ * CSA_FLAG_NO_SCORE in opt->flags sizes it for out_score = NULL. */
+size_t csa_grouped_workspace_bytes(const csa_desc *desc, int32_t m, int32_t k,
+                                   const csa_group_options *gopt, const csa_options *opt);
+
+/* ------------------------------------------------------------------------
  * Sparse attention over the selected keys.
  *
  * Operation (StreamIndex: Memory-Bounded Compressed Sparse Attention via

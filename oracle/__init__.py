@@ -27,7 +27,8 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRCS = [os.path.join(_HERE, "csa_oracle.c"), os.path.join(_HERE, "csa_attn_oracle.c")]
+_SRCS = [os.path.join(_HERE, "csa_oracle.c"), os.path.join(_HERE, "csa_attn_oracle.c"),
+         os.path.join(_HERE, "csa_group_oracle.c")]
 _LIB_PATH = os.path.join(_HERE, "libcsa_oracle.so")
 
 DTYPE_CODES = {"bf16": 0, "e4m3fn": 1, "f32": 2}
@@ -75,6 +76,11 @@ def _load():
     lib.csa_oracle_sparse_attention.argtypes = [p, p, p, p, i64, i64, i32, i32, i32,
                                                 ctypes.c_double, i32, p, p, p]
     lib.csa_oracle_sparse_attention.restype = i32
+    lib.csa_oracle_grouped.argtypes = [p, p, p, i64, i64, i32, i32, i32, i32, i32, i32, i64, p,
+                                       i64, i32, p, p]
+    lib.csa_oracle_grouped.restype = i32
+    lib.csa_oracle_group_pool.argtypes = [p, p, i64, i32, i32, i32, i64, p, p]
+    lib.csa_oracle_group_pool.restype = i64
     _lib = lib
     return lib
 
@@ -134,6 +140,47 @@ def topk_rows(q_rows, w_rows, k_keys, t_rows, m, topk, *, dtype="bf16",
     if rc != 0:
         raise RuntimeError("csa_oracle_rows failed")
     return out_idx, out_score
+
+
+def grouped_rows(q_entry, w_entry, k_keys, rows, m, topk, group, candidates, *, row_offset=0,
+                 nthreads=None):
+    """The grouped (approximate) top-k of rows ``rows`` of one batch entry
+    (csa_group_oracle.c): q_entry [S, H, D] bf16 bits (uint16) and w_entry
+    [S, H] float32 for every row of the entry, k_keys [T, D] bf16 bits.
+    Returns (idx int32 [n, k], score float64 [n, k])."""
+    lib = _load()
+    q_entry, qp = _arr(q_entry, np.uint16)
+    w_entry, wp = _arr(w_entry, np.float32)
+    k_keys, kp = _arr(k_keys, np.uint16)
+    rows, rp = _arr(rows, np.int64)
+    S, H, D = q_entry.shape
+    T = k_keys.shape[0]
+    n = rows.shape[0]
+    out_idx = np.empty((n, topk), np.int32)
+    out_score = np.empty((n, topk), np.float64)
+    if nthreads is None:
+        nthreads = min(16, os.cpu_count() or 1)
+    rc = lib.csa_oracle_grouped(qp, wp, kp, S, T, H, D, int(m), int(topk), int(group),
+                                int(candidates), int(row_offset), rp, n, int(nthreads),
+                                out_idx.ctypes.data_as(ctypes.c_void_p),
+                                out_score.ctypes.data_as(ctypes.c_void_p))
+    if rc != 0:
+        raise RuntimeError("csa_oracle_grouped failed")
+    return out_idx, out_score
+
+
+def group_pool(q_entry, w_entry, group, row):
+    """The pooled query of the group holding ``row`` (csa_group_oracle.c):
+    (pq float64 [H, D] bfloat16 values, pw float64 [H])."""
+    lib = _load()
+    q_entry, qp = _arr(q_entry, np.uint16)
+    w_entry, wp = _arr(w_entry, np.float32)
+    S, H, D = q_entry.shape
+    pq = np.empty((H, D), np.float64)
+    pw = np.empty(H, np.float64)
+    lib.csa_oracle_group_pool(qp, wp, S, H, D, int(group), int(row),
+                              pq.ctypes.data_as(ctypes.c_void_p), pw.ctypes.data_as(ctypes.c_void_p))
+    return pq, pw
 
 
 def score_pairs(q_rows, w_rows, k_keys, row, key, *, dtype="bf16",

@@ -29,7 +29,8 @@ CSA_FP8_E4M3FN = 1
 
 CSA_FLAG_NO_SCORE = 1
 
-EXPORTS = ("csa_index", "csa_index_ex", "csa_index_static", "csa_workspace_bytes", "csa_plan_query",
+EXPORTS = ("csa_index", "csa_index_ex", "csa_index_static", "csa_index_grouped",
+           "csa_grouped_workspace_bytes", "csa_workspace_bytes", "csa_plan_query",
            "csa_status_string", "csa_sparse_attention", "csa_sparse_attention_ex",
            "csa_sparse_attention_workspace_bytes")
 
@@ -55,6 +56,11 @@ class CsaPlanInfo(ctypes.Structure):
                 ("grid", ctypes.c_int32), ("key_splits", ctypes.c_int32),
                 ("n_blocks", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
                 ("keys_per_range", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class CsaGroupOptions(ctypes.Structure):
+    _fields_ = [("group", ctypes.c_int32), ("candidates", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 2)]
 
 
 class CsaAttnDesc(ctypes.Structure):
@@ -95,6 +101,14 @@ def load_library():
     lib.csa_index_ex.restype = ctypes.c_int
     lib.csa_index_static.argtypes = lib.csa_index_ex.argtypes
     lib.csa_index_static.restype = ctypes.c_int
+    lib.csa_index_grouped.argtypes = [vp, vp, vp, ctypes.POINTER(CsaDesc), i32, i32,
+                                      ctypes.POINTER(CsaGroupOptions), vp, vp,
+                                      ctypes.POINTER(CsaOptions), vp]
+    lib.csa_index_grouped.restype = ctypes.c_int
+    lib.csa_grouped_workspace_bytes.argtypes = [ctypes.POINTER(CsaDesc), i32, i32,
+                                                ctypes.POINTER(CsaGroupOptions),
+                                                ctypes.POINTER(CsaOptions)]
+    lib.csa_grouped_workspace_bytes.restype = ctypes.c_size_t
     lib.csa_workspace_bytes.argtypes = [ctypes.POINTER(CsaDesc), i32, i32,
                                         ctypes.POINTER(CsaOptions)]
     lib.csa_workspace_bytes.restype = ctypes.c_size_t
@@ -250,6 +264,81 @@ def index(q: torch.Tensor, w: torch.Tensor, k_cmp: torch.Tensor, m: int, k: int,
     if rc != CSA_OK:
         raise CsaError(rc, "csa_index_static" if static_scratch else "csa_index_ex")
     return out_idx, out_score
+
+
+def make_group_options(group: int, candidates: int = 0) -> CsaGroupOptions:
+    g = CsaGroupOptions()
+    g.group = int(group)
+    g.candidates = int(candidates)
+    return g
+
+
+def grouped_workspace_bytes(desc: CsaDesc, m: int, k: int, gopt: CsaGroupOptions,
+                            opt: Optional[CsaOptions] = None) -> int:
+    return int(load_library().csa_grouped_workspace_bytes(
+        ctypes.byref(desc), int(m), int(k), ctypes.byref(gopt),
+        ctypes.byref(opt) if opt is not None else None))
+
+
+def index_grouped(q: torch.Tensor, w: torch.Tensor, k_cmp: torch.Tensor, m: int, k: int,
+                  group: int, candidates: int = 0, *, out_idx: Optional[torch.Tensor] = None,
+                  out_score: Optional[torch.Tensor] = None, want_score: bool = True,
+                  row_offset: int = 0, chunk_keys: int = 0,
+                  workspace: Optional[torch.Tensor] = None, timing=None,
+                  stream: Optional[torch.cuda.Stream] = None):
+    """The grouped (approximate) indexer (csa_index_grouped): groups of
+    `group` consecutive positions share one scan by their pooled query,
+    which keeps `candidates` keys (0 = min(2k, 8192)); each member re-ranks
+    them and its own extra keys exactly.  bf16, H = 64, D = 128.  Returns
+    (out_idx, out_score or None)."""
+    lib = load_library()
+    for t, name in ((q, "q"), (k_cmp, "k_cmp")):
+        _check(t, name, torch.bfloat16)
+    _check(w, "w", torch.float32)
+    B, S, H, D = q.shape
+    T = k_cmp.shape[1]
+    if tuple(w.shape) != (B, S, H) or tuple(k_cmp.shape) != (B, T, D):
+        raise ValueError("inconsistent shapes of q, w, k_cmp")
+    if out_idx is None:
+        out_idx = torch.empty((B, S, k), dtype=torch.int32, device=q.device)
+    if want_score and out_score is None:
+        out_score = torch.empty((B, S, k), dtype=torch.float32, device=q.device)
+    if not want_score and out_score is not None:
+        raise ValueError("out_score given with want_score=False")
+    _check(out_idx, "out_idx", torch.int32)
+    if out_score is not None:
+        _check(out_score, "out_score", torch.float32)
+    desc = make_desc(B, S, T, H, D)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _check(workspace, "workspace")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    opt = make_options(chunk_keys, row_offset, 0, ws_ptr, ws_bytes,
+                       timing if timing is not None else (None, None))
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    g = make_group_options(group, candidates)
+    rc = lib.csa_index_grouped(q.data_ptr(), w.data_ptr(), k_cmp.data_ptr(), ctypes.byref(desc),
+                               int(m), int(k), ctypes.byref(g), out_idx.data_ptr(),
+                               out_score.data_ptr() if out_score is not None else None,
+                               ctypes.byref(opt), ctypes.c_void_p(stream.cuda_stream))
+    if rc != CSA_OK:
+        raise CsaError(rc, "csa_index_grouped")
+    return out_idx, out_score
+
+
+def grouped_workspace_for(q: torch.Tensor, k_cmp: torch.Tensor, m: int, k: int, group: int,
+                          candidates: int = 0, row_offset: int = 0, chunk_keys: int = 0,
+                          want_score: bool = True) -> torch.Tensor:
+    """A torch-allocated workspace for `index_grouped` on these inputs."""
+    B, S, H, D = q.shape
+    n = grouped_workspace_bytes(make_desc(B, S, k_cmp.shape[1], H, D), m, k,
+                                make_group_options(group, candidates),
+                                make_options(chunk_keys, row_offset,
+                                             flags=0 if want_score else CSA_FLAG_NO_SCORE))
+    if n == 0:
+        raise CsaError(CSA_ERR_INVALID_ARG, "csa_grouped_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=q.device)
 
 
 def make_attn_desc(B, S, T, H, D, n_sel) -> CsaAttnDesc:

@@ -17,9 +17,10 @@ LIB = os.path.join(HERE, "libcsa_index.so")
 OBJDIR = os.path.join(HERE, "_build")
 
 # the scoring-kernel instantiations first: they take longest
-SOURCES = ["csa_stream_bf16_d128.hip", "csa_stream_fp8_d128.hip", "csa_stream_bf16_d64.hip",
-           "csa_stream_fp8_d64.hip", "csa_stream_bf16_d32.hip", "csa_kernels.hip", "csa_attn.hip",
-           "csa_sort.hip", "csa_plan.cpp", "csa_abi.cpp", "csa_static.hip"]
+SOURCES = ["csa_stream_bf16_d128.hip", "csa_stream_list.hip", "csa_stream_fp8_d128.hip",
+           "csa_stream_bf16_d64.hip", "csa_stream_fp8_d64.hip", "csa_stream_bf16_d32.hip",
+           "csa_kernels.hip", "csa_attn.hip", "csa_sort.hip", "csa_plan.cpp", "csa_abi.cpp",
+           "csa_static.hip", "csa_group.hip", "csa_grouped.cpp"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -12,11 +12,12 @@
 #include <cstdio>
 #include <cstdlib>
 
+#include "csa_abi_internal.hpp"
 #include "csa_index.h"
 #include "csa_kernels.hpp"
 #include "csa_plan.hpp"
 
-namespace {
+namespace csa {
 
 int device_cus(int *out)
 {
@@ -30,23 +31,44 @@ int device_cus(int *out)
     return CSA_OK;
 }
 
+}  // namespace csa
+
+namespace {
+
+using csa::device_cus;
+
 int plan_for(const csa_desc *desc, int32_t m, int32_t k, const csa_options *opt,
              csa::Plan *p, int *cus, bool no_score = false)
 {
+    return csa::plan_call(desc, m, k, opt, p, cus, no_score, 1);
+}
+
+}  // namespace
+
+namespace csa {
+
+int plan_call(const csa_desc *desc, int32_t m, int32_t k, const csa_options *opt, Plan *p,
+              int *cus, bool no_score, int64_t pos_mul)
+{
     int num_cus = (opt && opt->num_cus > 0) ? opt->num_cus : 0;
     if (opt && opt->num_cus < 0) return CSA_ERR_INVALID_ARG;
-    // validate everything that does not need the device before asking it
-    const int pre = csa::make_plan(desc, m, k, opt, num_cus > 0 ? num_cus : 1, p, no_score);
+    const int pre = make_plan(desc, m, k, opt, num_cus > 0 ? num_cus : 1, p, no_score, pos_mul);
     if (pre != CSA_OK) return pre;
     if (num_cus == 0) {
         const int rc = device_cus(&num_cus);
         if (rc != CSA_OK) return rc;
     }
     *cus = num_cus;
-    return csa::make_plan(desc, m, k, opt, num_cus, p, no_score);
+    return make_plan(desc, m, k, opt, num_cus, p, no_score, pos_mul);
 }
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+}  // namespace csa
+
+namespace {
+
+using csa::aligned;
 
 // CSA_LOG set to anything but "" or "0": each call prints its plan to stderr.
 bool log_plans()
@@ -117,6 +139,72 @@ extern "C" size_t csa_workspace_bytes(const csa_desc *desc, int32_t m, int32_t k
     return p.ws_bytes;
 }
 
+namespace csa {
+
+// Enqueues a planned call: the scoring kernel, the merge of the key ranges'
+// lists and the row sort, as the plan asks.  ws holds p.ws_bytes bytes.
+int run_index(const Plan &p, int cus, const void *q, const float *w, const void *k_cmp,
+              const float *q_scale, const float *k_scale, int32_t *out_idx, float *out_score,
+              void *ws, const hipEvent_t *timing, hipStream_t stream, const ListArgs *lists)
+{
+    StreamArgs a;
+    a.q = static_cast<const unsigned char *>(q);
+    a.w = w;
+    a.k = static_cast<const unsigned char *>(k_cmp);
+    a.q_scale = q_scale;
+    a.k_scale = k_scale;
+    a.out_idx = out_idx;
+    // without a score output, a separate row sort keeps the scores in the workspace
+    float *const scores = out_score ? out_score
+        : (p.sort_e == 0 ? reinterpret_cast<float *>(static_cast<unsigned char *>(ws) + p.score_offset)
+                         : nullptr);
+    a.out_score = scores;
+    a.ws = static_cast<uint32_t *>(ws);
+    // unsorted lists: the ranges' partial lists, or with one range the output
+    // rows themselves (sorted afterwards by the row sort)
+    unsigned char *part = static_cast<unsigned char *>(ws) + p.part_offset;
+    a.part_idx = p.n_splits > 1 ? reinterpret_cast<int32_t *>(part) : out_idx;
+    a.part_score = p.n_splits > 1
+        ? reinterpret_cast<float *>(part + size_t(p.B * p.S) * size_t(p.n_splits) * size_t(p.k) * 4u)
+        : scores;
+    a.B = p.B;
+    a.S = p.S;
+    a.T = p.T;
+    a.row_offset = p.row_offset;
+    a.m = p.m;
+    a.topk = p.k;
+    a.log_cap = p.log_cap;
+    a.n_splits = p.n_splits;
+    a.split_keys = p.n_splits > 1 ? p.split_keys : int(kMaxKeys);
+    a.blocks_per_batch = p.blocks_per_batch;
+    a.n_units = p.n_units;
+    a.sort_e = p.sort_e;
+    a.key_tile = p.key_tile;
+    a.pos_mul = p.pos_mul;
+    a.klist = lists ? lists->klist : nullptr;
+    a.klen = lists ? lists->klen : nullptr;
+    a.n_lists = lists ? lists->n_lists : 0;
+    a.list_cap = lists ? lists->list_cap : 0;
+    a.list_rows = lists ? lists->list_rows : 0;
+
+    int rc = CSA_OK;
+    if (timing && timing[0] && hipEventRecord(timing[0], stream) != hipSuccess) rc = CSA_ERR_HIP;
+    const hipError_t e = lists ? (p.grid > 0 ? launch_stream_list(a, p.grid, stream) : hipSuccess)
+                               : launch_stream_topk(p, a, stream);
+    if (rc == CSA_OK && e != hipSuccess) rc = CSA_ERR_HIP;
+    if (rc == CSA_OK && timing && timing[1] && hipEventRecord(timing[1], stream) != hipSuccess)
+        rc = CSA_ERR_HIP;
+    if (rc == CSA_OK &&
+        launch_merge_splits(p, a.part_idx, a.part_score, out_idx, scores, cus, stream) != hipSuccess)
+        rc = CSA_ERR_HIP;
+    if (rc == CSA_OK && p.sort_e == 0 &&
+        launch_sort_rows(p, out_idx, scores, cus, stream) != hipSuccess)
+        rc = CSA_ERR_HIP;
+    return rc;
+}
+
+}  // namespace csa
+
 extern "C" int csa_index_ex(const void *q, const float *w, const void *k_cmp,
                             const csa_desc *desc, int32_t m, int32_t k,
                             int32_t *out_idx, float *out_score,
@@ -146,54 +234,8 @@ extern "C" int csa_index_ex(const void *q, const float *w, const void *k_cmp,
         if (hipMallocAsync(&ws, p.ws_bytes, stream) != hipSuccess) return CSA_ERR_HIP;
         owned = true;
     }
-
-    csa::StreamArgs a;
-    a.q = static_cast<const unsigned char *>(q);
-    a.w = w;
-    a.k = static_cast<const unsigned char *>(k_cmp);
-    a.q_scale = desc->q_scale;
-    a.k_scale = desc->k_scale;
-    a.out_idx = out_idx;
-    // without a score output, a separate row sort keeps the scores in the workspace
-    float *const scores = out_score ? out_score
-        : (p.sort_e == 0 ? reinterpret_cast<float *>(static_cast<unsigned char *>(ws) + p.score_offset)
-                         : nullptr);
-    a.out_score = scores;
-    a.ws = static_cast<uint32_t *>(ws);
-    // unsorted lists: the ranges' partial lists, or with one range the output
-    // rows themselves (sorted afterwards by the row sort)
-    unsigned char *part = static_cast<unsigned char *>(ws) + p.part_offset;
-    a.part_idx = p.n_splits > 1 ? reinterpret_cast<int32_t *>(part) : out_idx;
-    a.part_score = p.n_splits > 1
-        ? reinterpret_cast<float *>(part + size_t(p.B * p.S) * size_t(p.n_splits) * size_t(p.k) * 4u)
-        : scores;
-    a.B = p.B;
-    a.S = p.S;
-    a.T = p.T;
-    a.row_offset = p.row_offset;
-    a.m = p.m;
-    a.topk = p.k;
-    a.log_cap = p.log_cap;
-    a.n_splits = p.n_splits;
-    a.split_keys = p.n_splits > 1 ? p.split_keys : int(csa::kMaxKeys);
-    a.blocks_per_batch = p.blocks_per_batch;
-    a.n_units = p.n_units;
-    a.sort_e = p.sort_e;
-    a.key_tile = p.key_tile;
-
-    rc = CSA_OK;
-    if (opt && opt->timing[0] && hipEventRecord(opt->timing[0], stream) != hipSuccess)
-        rc = CSA_ERR_HIP;
-    if (rc == CSA_OK && csa::launch_stream_topk(p, a, stream) != hipSuccess) rc = CSA_ERR_HIP;
-    if (rc == CSA_OK && opt && opt->timing[1] && hipEventRecord(opt->timing[1], stream) != hipSuccess)
-        rc = CSA_ERR_HIP;
-    if (rc == CSA_OK &&
-        csa::launch_merge_splits(p, a.part_idx, a.part_score, out_idx, scores, cus, stream) !=
-            hipSuccess)
-        rc = CSA_ERR_HIP;
-    if (rc == CSA_OK && p.sort_e == 0 &&
-        csa::launch_sort_rows(p, out_idx, scores, cus, stream) != hipSuccess)
-        rc = CSA_ERR_HIP;
+    rc = csa::run_index(p, cus, q, w, k_cmp, desc->q_scale, desc->k_scale, out_idx, out_score, ws,
+                        opt ? opt->timing : nullptr, stream, nullptr);
     if (owned && hipFreeAsync(ws, stream) != hipSuccess && rc == CSA_OK) rc = CSA_ERR_HIP;
     return rc;
 }

@@ -27,9 +27,19 @@ struct StreamArgs {
     int64_t blocks_per_batch, n_units;
     int sort_e;                 // > 0: rows sorted in the kernel, sort_e keys per lane
     int key_tile;               // keys staged in LDS per workgroup step
+    int64_t pos_mul;            // q row i is position row_offset + i * pos_mul (1: rows)
+    // key lists (grouped re-rank): list l holds ascending key indices for
+    // list_rows consecutive rows, list_cap entries (a multiple of the key
+    // tile, INT32_MAX past its klen[l] valid ones)
+    const int32_t *klist;       // [B, n_lists, list_cap] or null
+    const int32_t *klen;        // [B, n_lists]
+    int64_t n_lists;
+    int list_cap, list_rows;
 };
 
 hipError_t launch_stream_topk(const Plan &p, const StreamArgs &a, hipStream_t s);
+// The scoring kernel over key lists (bf16, H = 64, D = 128, sorted rows).
+hipError_t launch_stream_list(const StreamArgs &a, int grid, hipStream_t s);
 // per operand type and head dimension (csa_stream_*.hip)
 hipError_t launch_stream_bf16_d32(int H, const StreamArgs &a, int grid, hipStream_t s);
 hipError_t launch_stream_bf16_d64(int H, const StreamArgs &a, int grid, hipStream_t s);

@@ -38,9 +38,10 @@ static int64_t next_pow2(int64_t x)
 }
 
 int make_plan(const csa_desc *desc, int32_t m, int32_t k,
-              const csa_options *opt, int num_cus, Plan *plan, bool no_score)
+              const csa_options *opt, int num_cus, Plan *plan, bool no_score, int64_t pos_mul)
 {
-    if (!desc || !plan || num_cus <= 0) return CSA_ERR_INVALID_ARG;
+    if (!desc || !plan || num_cus <= 0 || pos_mul < 1 || pos_mul > (int64_t(1) << 20))
+        return CSA_ERR_INVALID_ARG;
     if (desc->B < 1 || desc->S < 0 || desc->T < 0) return CSA_ERR_INVALID_ARG;
     // key indices and the kernels' key arithmetic (tile ends, key ranges) are
     // 32-bit: T <= 2^30 keeps every such sum below 2^31
@@ -72,7 +73,8 @@ int make_plan(const csa_desc *desc, int32_t m, int32_t k,
         splits_req = opt->key_splits;
     }
     // positions must stay representable: t + 1 fits comfortably in int64
-    if (desc->S > (int64_t(1) << 40) || row_offset > (int64_t(1) << 40))
+    if (desc->S > (int64_t(1) << 40) || row_offset > (int64_t(1) << 40) ||
+        desc->S * pos_mul > (int64_t(1) << 41))
         return CSA_ERR_INVALID_ARG;
     // element counts must fit the 64-bit offsets used by the kernels (checked
     // before multiplying: a signed overflow would already be undefined)
@@ -104,7 +106,8 @@ int make_plan(const csa_desc *desc, int32_t m, int32_t k,
     const int64_t resident = int64_t(num_cus);  // one 8-wave workgroup per CU
 
     // key ranges: requested, or automatic when the query blocks leave CUs idle
-    const int64_t n_max = desc->S > 0 ? std::min<int64_t>(desc->T, (row_offset + desc->S) / m) : 0;
+    const int64_t last_pos = row_offset + (desc->S - 1) * pos_mul;  // position of the last row
+    const int64_t n_max = desc->S > 0 ? std::min<int64_t>(desc->T, (last_pos + 1) / m) : 0;
     const int64_t tiles = (n_max + kKeysPerTile - 1) / kKeysPerTile;
     int64_t G = 1;
     if (splits_req > 0) {
@@ -143,6 +146,7 @@ int make_plan(const csa_desc *desc, int32_t m, int32_t k,
         return CSA_ERR_UNSUPPORTED;
     p.key_tile = key_tile;
     p.no_score = no_score;
+    p.pos_mul = pos_mul;
     const size_t per_wave = size_t(p.QW) * size_t(p.log_cap) * 8u;  // u32 key + i32 index
     const size_t logs = (size_t(p.grid) * kWaves * per_wave + 255) / 256 * 256;
     p.part_offset = logs;

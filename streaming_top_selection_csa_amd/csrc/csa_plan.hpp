@@ -55,6 +55,7 @@ struct Plan {
     int sort_e = 0;             // > 0: the scoring kernel sorts the rows (sort_e keys per lane)
     int key_tile = kKeysPerTile;  // keys staged in LDS per workgroup step
     bool no_score = false;      // the caller passes no score output
+    int64_t pos_mul = 1;        // q row i is position row_offset + i * pos_mul
     size_t part_offset = 0;     // byte offset of the partial lists (G > 1)
     size_t score_offset = 0;    // byte offset of the score rows a separate sort needs
     size_t ws_bytes = 0;        // 256-aligned
@@ -69,7 +70,10 @@ int default_key_tile(int H, int D);
 // Validates every argument and fills `plan`.  num_cus must be > 0.
 // no_score: the call writes no scores (also implied by CSA_FLAG_NO_SCORE).
 // Returns CSA_OK or a negative csa_status; never throws.
+// pos_mul: q row i is position row_offset + i * pos_mul (the grouped scan's
+// pooled rows stand for every pos_mul-th position).
 int make_plan(const csa_desc *desc, int32_t m, int32_t k,
-              const csa_options *opt, int num_cus, Plan *plan, bool no_score = false);
+              const csa_options *opt, int num_cus, Plan *plan, bool no_score = false,
+              int64_t pos_mul = 1);
 
 }  // namespace csa

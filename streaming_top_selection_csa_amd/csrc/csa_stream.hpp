@@ -952,7 +952,12 @@ struct Epi {
 // output row itself with one range) for the merge and sort passes.
 // Otherwise units are query blocks and each row leaves the kernel sorted
 // (next_pow2(k) <= kStageSlots).
-template <int H, int D, bool FP8, bool SPLIT, int KT = kKeysPerTile>
+// LIST: the keys of a query block are not a prefix of k_cmp but a list of
+// key indices in ascending order (a.klist), shared by a.list_rows
+// consecutive query rows; a row still only accepts keys below its visible
+// count.  Used by the grouped (approximate) entry point to re-rank shared
+// candidates.
+template <int H, int D, bool FP8, bool SPLIT, int KT = kKeysPerTile, bool LIST = false>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 stream_topk_kernel(StreamArgs a)
 {
@@ -967,6 +972,7 @@ stream_topk_kernel(StreamArgs a)
     constexpr int CT = 64;
     static_assert(KT == 32 || KT % CT == 0, "key tile: 32 or a multiple of 64 keys");
     static_assert(!FP8 || KT >= CT, "fp8 key scales are staged 64 at a time");
+    static_assert(!LIST || (!FP8 && !SPLIT && KT >= CT), "key lists: bf16 sorted rows");
     constexpr int NSUB = KT >= CT ? KT / CT : 1;     // compute tiles per staged tile
     constexpr bool HALF_TILES = KT < CT;             // a staged tile is one half
     constexpr int NDS = D / O::KSTEP;                // K steps per half tile
@@ -1034,8 +1040,12 @@ stream_topk_kernel(StreamArgs a)
         const int64_t p_last = (p0 + QB < a.S ? p0 + QB : a.S) - 1;
         // keys [klo, n_hi) of this unit: all visible keys, or one key range
         const int klo = SPLIT ? js * a.split_keys : 0;
-        int n_hi = int(n_visible(a.row_offset + p_last, a.T, a.m));
+        int n_hi = int(n_visible(a.row_offset + p_last * a.pos_mul, a.T, a.m));
         if (SPLIT && klo + a.split_keys < n_hi) n_hi = klo + a.split_keys;
+        // with key lists, the tiles cover list positions [0, length)
+        const int32_t *const klist = LIST ? a.klist + (b * a.n_lists + p0 / a.list_rows) * a.list_cap
+                                          : nullptr;
+        if constexpr (LIST) n_hi = a.klen[b * a.n_lists + p0 / a.list_rows];
         const int64_t wp0 = p0 + int64_t(wave) * QW;
 
         // ---- the wave's 64 (position, head) rows of q and their weights
@@ -1069,7 +1079,7 @@ stream_topk_kernel(StreamArgs a)
 #pragma unroll
         for (int qi = 0; qi < QW; ++qi) {
             const int64_t pos = wp0 + qi;
-            nv[qi] = pos < a.S ? int(n_visible(a.row_offset + pos, a.T, a.m)) : 0;
+            nv[qi] = pos < a.S ? int(n_visible(a.row_offset + pos * a.pos_mul, a.T, a.m)) : 0;
             if (SPLIT && nv[qi] > n_hi) nv[qi] = n_hi;  // the end of the key range
             tau[qi] = 0u;  // below the key of any finite score: accept all
             cnt[qi] = 0;
@@ -1081,13 +1091,13 @@ stream_topk_kernel(StreamArgs a)
 
         // Filter the wave's scores against key tile `it` and append the
         // survivors to the candidate logs (see the threshold histogram).
-        auto consume = [&](const float (&sc)[QW], int it) {
+        auto consume = [&](const float (&sc)[QW], int it, int list_key) {
             const int kt = klo + it * CT;
-            const int key = kt + lane;
+            const int key = LIST ? list_key : kt + lane;
 #pragma unroll
             for (int qi = 0; qi < QW; ++qi) {
                 const int r = qi;
-                if (kt >= nv[qi]) continue;  // wave-uniform
+                if (!LIST && kt >= nv[qi]) continue;  // wave-uniform
                 const uint32_t u = order_key(sc[r]);
                 const bool pass = key < nv[qi] && u > tau[qi];
                 const uint64_t mk = __ballot(pass);
@@ -1153,12 +1163,25 @@ stream_topk_kernel(StreamArgs a)
         const unsigned char *kbase = a.k + b * a.T * (D * O::ESZ);
         const float *ksbase = FP8 ? a.k_scale + b * a.T : nullptr;
         // DMA loads this wave issues per tile (the vmcnt it waits on); with
-        // fp8, waves 0 .. NSUB-1 also load 64 key scales each
+        // fp8 (key scales) or key lists (key indices), waves 0 .. NSUB-1 also
+        // load 64 words each
         const int my_dma = (NDMA > wave ? (NDMA - wave + kWaves - 1) / kWaves : 0) +
-                           ((FP8 && wave < NSUB) ? 1 : 0);
+                           (((FP8 || LIST) && wave < NSUB) ? 1 : 0);
+        // key lists: the key index of each row this lane stages, fetched one
+        // staged tile ahead of its DMA (list entries past the end hold
+        // INT32_MAX and stage row T-1)
+        int32_t lrow[NDMA_W];
+        auto fetch_rows = [&](int st) {
+#pragma unroll
+            for (int v = 0; v < NDMA_W; ++v) {
+                const int j = wave + v * kWaves;
+                const int r = (j * 1024 + lane * 16) / ROWB;
+                lrow[v] = (j < NDMA && st * KT < a.list_cap) ? klist[st * KT + r] : 0;
+            }
+        };
         auto dma_tile = [&](int st, int buf) {
             const int64_t row0 = int64_t(klo) + int64_t(st) * KT;
-            const unsigned char *tb = kbase + row0 * ROWB;  // first key row of the tile
+            const unsigned char *tb = kbase + (LIST ? 0 : row0 * ROWB);  // first key row of the tile
             // rows past T are never used: they repeat row T-1
             const int rmax = a.T - row0 - 1 < KT - 1 ? int(a.T - row0 - 1) : KT - 1;
 #pragma unroll
@@ -1168,11 +1191,22 @@ stream_topk_kernel(StreamArgs a)
                     const int off = j * 1024 + lane * 16;  // LDS byte of this lane
                     const int r = off / ROWB;
                     const int c = ((off % ROWB) / 16) ^ (r % NC);
-                    const uint32_t src = uint32_t(r < rmax ? r : rmax) * ROWB + uint32_t(c * 16);
+                    uint32_t row = uint32_t(r < rmax ? r : rmax);
+                    if constexpr (LIST) row = uint32_t(lrow[v] < a.T ? lrow[v] : a.T - 1);
+                    const uint64_t src = uint64_t(row) * ROWB + uint32_t(c * 16);
                     __builtin_amdgcn_global_load_lds(
                         tb + src,
                         (__attribute__((address_space(3))) void *)&s_k[buf][j * 1024], 16, 0, 0);
                 }
+            }
+            if constexpr (LIST) {
+                // the tile's key indices, for the filter
+                if (wave < NSUB)
+                    __builtin_amdgcn_global_load_lds(
+                        klist + row0 + wave * CT + lane,
+                        (__attribute__((address_space(3))) void *)&s_ks[buf][wave * CT], 4, 0, 0);
+                // the next staged tile's rows
+                fetch_rows(st + 1);
             }
             if constexpr (FP8) {
                 if (wave < NSUB) {
@@ -1240,7 +1274,8 @@ stream_topk_kernel(StreamArgs a)
             if constexpr (FP8)
 #pragma unroll
                 for (int qi = 0; qi < QW; ++qi) sc[qi] *= ksv;
-            consume(sc, it);
+            // with key lists, ksv carries the lane's key index
+            consume(sc, it, LIST ? __float_as_int(ksv) : 0);
         };
 
         // Waves 0-3 run, per compute tile i: MFMA(half 0), its epilogue,
@@ -1254,6 +1289,7 @@ stream_topk_kernel(StreamArgs a)
         const int nst = n_hi > klo ? (n_hi - klo + KT - 1) / KT : 0;     // staged tiles
         // every wave is past its last read of the ring (previous block)
         __syncthreads();
+        if constexpr (LIST) fetch_rows(0);
         for (int t = 0; t < PD && t < nst; ++t) dma_tile(t, t);
         sync_tiles(later_loads(-1, nst));
         float ksv_prev = 1.f;
@@ -1266,7 +1302,7 @@ stream_topk_kernel(StreamArgs a)
             const int buf = st % NBUF;
             const int r0 = HALF_TILES ? 0 : (it % NSUB) * CT;
             float ksv = 1.f;
-            if constexpr (FP8) ksv = s_ks[buf][r0 + lane];
+            if constexpr (FP8 || LIST) ksv = s_ks[buf][r0 + lane];
             // Each wave stages its share of tile st+PD (over tile st-1, which
             // every wave has finished) after its own filter step, so that the
             // leading and the lagging waves issue their loads half a tile

@@ -12,6 +12,7 @@
 #include <cstdlib>
 #include <random>
 
+#include "csa_group.hpp"
 #include "csa_index.h"
 #include "csa_kernels.hpp"
 
@@ -53,6 +54,22 @@ hipError_t launch_sort_rows(const Plan &, int32_t *, float *, int, hipStream_t)
 hipError_t launch_sparse_attention(const AttnArgs &, int, int, hipStream_t)
 {
     ++g_launches;
+    return hipErrorInvalidValue;
+}
+hipError_t launch_stream_list(const StreamArgs &, int, hipStream_t)
+{
+    ++g_launches;
+    return hipErrorInvalidValue;
+}
+hipError_t launch_pool_queries(const void *, const float *, void *, float *, int64_t, int64_t,
+                               int, int, int, int, hipStream_t)
+{
+    ++g_launches;
+    return hipErrorInvalidValue;
+}
+hipError_t launch_build_lists(const int32_t *, int32_t *, int32_t *, int64_t, int64_t, int64_t,
+                              int64_t, int, int, int, int, int, hipStream_t)
+{
     return hipErrorInvalidValue;
 }
 }  // namespace csa
@@ -121,6 +138,19 @@ int main(int argc, char **argv)
         const int rx = csa_index_ex(p, static_cast<const float *>(p), p, &d, m, k,
                                     static_cast<int32_t *>(p), static_cast<float *>(p), op, nullptr);
         if (rc != CSA_OK && rx != rc) fail("csa_index_ex disagrees with the plan's status", i);
+
+        // ---- grouped indexer (same arguments plus a group and a candidate count)
+        csa_group_options go{};
+        const int32_t gs[] = {8, 16, 64, 0, 7, 12, -8, 1 << 20};
+        go.group = gs[rng() % 8];
+        go.candidates = (rng() & 1) ? 0 : pick32();
+        go.reserved[0] = (rng() % 32 == 0) ? 1 : 0;
+        const size_t gws = csa_grouped_workspace_bytes(&d, m, k, &go, op);
+        const int rg = csa_index_grouped(p, static_cast<const float *>(p), p, &d, m, k, &go,
+                                         static_cast<int32_t *>(p), (rng() & 1) ? nullptr
+                                         : static_cast<float *>(p), op, nullptr);
+        if (gws == 0 && rg == CSA_OK && d.S > 0) fail("grouped call ran without a workspace", i);
+        if (rc != CSA_OK && rg == CSA_OK) fail("grouped call accepted an invalid plan", i);
 
         // ---- sparse attention
         csa_attn_desc ad{};

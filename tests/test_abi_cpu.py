@@ -355,7 +355,8 @@ def test_host_code_fuzz_under_sanitizers(tmp_path):
            "-fno-sanitize-recover=all", "-D__HIP_PLATFORM_AMD__", "-I", rocm_inc,
            "-I", os.path.join(ROOT, "include"), "-I", csrc,
            os.path.join(ROOT, "tests", "fuzz_abi_host.cpp"), os.path.join(csrc, "csa_plan.cpp"),
-           os.path.join(csrc, "csa_abi.cpp"), "-o", str(exe)]
+           os.path.join(csrc, "csa_abi.cpp"), os.path.join(csrc, "csa_grouped.cpp"), "-o",
+           str(exe)]
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-3000:]
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0", UBSAN_OPTIONS="print_stacktrace=1")
