@@ -189,8 +189,16 @@ int run_index(const Plan &p, int cus, const void *q, const float *w, const void 
 
     int rc = CSA_OK;
     if (timing && timing[0] && hipEventRecord(timing[0], stream) != hipSuccess) rc = CSA_ERR_HIP;
-    const hipError_t e = lists ? (p.grid > 0 ? launch_stream_list(a, p.grid, stream) : hipSuccess)
-                               : launch_stream_topk(p, a, stream);
+    hipError_t e = hipSuccess;
+    if (p.grid <= 0)
+        e = hipSuccess;
+    else if (lists)
+        e = launch_stream_list(a, p.grid, stream);
+    else if (p.pos_mul != 1)
+        e = (p.fp8 || p.H != 64 || p.D != 128) ? hipErrorInvalidValue
+                                               : launch_stream_pooled(a, p.grid, stream);
+    else
+        e = launch_stream_topk(p, a, stream);
     if (rc == CSA_OK && e != hipSuccess) rc = CSA_ERR_HIP;
     if (rc == CSA_OK && timing && timing[1] && hipEventRecord(timing[1], stream) != hipSuccess)
         rc = CSA_ERR_HIP;

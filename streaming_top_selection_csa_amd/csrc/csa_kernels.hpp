@@ -40,6 +40,8 @@ struct StreamArgs {
 hipError_t launch_stream_topk(const Plan &p, const StreamArgs &a, hipStream_t s);
 // The scoring kernel over key lists (bf16, H = 64, D = 128, sorted rows).
 hipError_t launch_stream_list(const StreamArgs &a, int grid, hipStream_t s);
+// The scoring kernel over pooled query rows (bf16, H = 64, D = 128).
+hipError_t launch_stream_pooled(const StreamArgs &a, int grid, hipStream_t s);
 // per operand type and head dimension (csa_stream_*.hip)
 hipError_t launch_stream_bf16_d32(int H, const StreamArgs &a, int grid, hipStream_t s);
 hipError_t launch_stream_bf16_d64(int H, const StreamArgs &a, int grid, hipStream_t s);

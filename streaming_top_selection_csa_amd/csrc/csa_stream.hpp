@@ -952,12 +952,16 @@ struct Epi {
 // output row itself with one range) for the merge and sort passes.
 // Otherwise units are query blocks and each row leaves the kernel sorted
 // (next_pow2(k) <= kStageSlots).
-// LIST: the keys of a query block are not a prefix of k_cmp but a list of
-// key indices in ascending order (a.klist), shared by a.list_rows
-// consecutive query rows; a row still only accepts keys below its visible
-// count.  Used by the grouped (approximate) entry point to re-rank shared
-// candidates.
-template <int H, int D, bool FP8, bool SPLIT, int KT = kKeysPerTile, bool LIST = false>
+// Kernel modes.  kPlain: q row i is position row_offset + i.  kPooled: q row
+// i stands for position row_offset + i * pos_mul (the grouped entry point's
+// pooled queries, one per group of pos_mul positions).  kList: the keys of
+// a query block are not a prefix of k_cmp but a list of key indices in
+// ascending order (a.klist), shared by a.list_rows consecutive query rows;
+// a row still only accepts keys below its visible count (the grouped
+// entry point's re-rank of shared candidates).
+enum { kPlain = 0, kPooled = 1, kList = 2 };
+
+template <int H, int D, bool FP8, bool SPLIT, int KT = kKeysPerTile, int MODE = kPlain>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 stream_topk_kernel(StreamArgs a)
 {
@@ -972,7 +976,11 @@ stream_topk_kernel(StreamArgs a)
     constexpr int CT = 64;
     static_assert(KT == 32 || KT % CT == 0, "key tile: 32 or a multiple of 64 keys");
     static_assert(!FP8 || KT >= CT, "fp8 key scales are staged 64 at a time");
+    constexpr bool LIST = MODE == kList;
     static_assert(!LIST || (!FP8 && !SPLIT && KT >= CT), "key lists: bf16 sorted rows");
+    // position of q row i
+    auto position = [&](int64_t i) { return MODE == kPooled ? a.row_offset + i * a.pos_mul
+                                                            : a.row_offset + i; };
     constexpr int NSUB = KT >= CT ? KT / CT : 1;     // compute tiles per staged tile
     constexpr bool HALF_TILES = KT < CT;             // a staged tile is one half
     constexpr int NDS = D / O::KSTEP;                // K steps per half tile
@@ -1040,7 +1048,7 @@ stream_topk_kernel(StreamArgs a)
         const int64_t p_last = (p0 + QB < a.S ? p0 + QB : a.S) - 1;
         // keys [klo, n_hi) of this unit: all visible keys, or one key range
         const int klo = SPLIT ? js * a.split_keys : 0;
-        int n_hi = int(n_visible(a.row_offset + p_last * a.pos_mul, a.T, a.m));
+        int n_hi = int(n_visible(position(p_last), a.T, a.m));
         if (SPLIT && klo + a.split_keys < n_hi) n_hi = klo + a.split_keys;
         // with key lists, the tiles cover list positions [0, length)
         const int32_t *const klist = LIST ? a.klist + (b * a.n_lists + p0 / a.list_rows) * a.list_cap
@@ -1079,7 +1087,7 @@ stream_topk_kernel(StreamArgs a)
 #pragma unroll
         for (int qi = 0; qi < QW; ++qi) {
             const int64_t pos = wp0 + qi;
-            nv[qi] = pos < a.S ? int(n_visible(a.row_offset + pos * a.pos_mul, a.T, a.m)) : 0;
+            nv[qi] = pos < a.S ? int(n_visible(position(pos), a.T, a.m)) : 0;
             if (SPLIT && nv[qi] > n_hi) nv[qi] = n_hi;  // the end of the key range
             tau[qi] = 0u;  // below the key of any finite score: accept all
             cnt[qi] = 0;
@@ -1191,12 +1199,18 @@ stream_topk_kernel(StreamArgs a)
                     const int off = j * 1024 + lane * 16;  // LDS byte of this lane
                     const int r = off / ROWB;
                     const int c = ((off % ROWB) / 16) ^ (r % NC);
-                    uint32_t row = uint32_t(r < rmax ? r : rmax);
-                    if constexpr (LIST) row = uint32_t(lrow[v] < a.T ? lrow[v] : a.T - 1);
-                    const uint64_t src = uint64_t(row) * ROWB + uint32_t(c * 16);
+                    const unsigned char *src;
+                    if constexpr (LIST) {
+                        // a listed key row anywhere in k_cmp: 64-bit offset
+                        const int64_t row = lrow[v] < a.T ? lrow[v] : a.T - 1;
+                        src = tb + row * ROWB + c * 16;
+                    } else {
+                        // a row of this tile: 32-bit offset from the tile's first row
+                        src = tb + (uint32_t(r < rmax ? r : rmax) * ROWB + uint32_t(c * 16));
+                    }
                     __builtin_amdgcn_global_load_lds(
-                        tb + src,
-                        (__attribute__((address_space(3))) void *)&s_k[buf][j * 1024], 16, 0, 0);
+                        src, (__attribute__((address_space(3))) void *)&s_k[buf][j * 1024], 16, 0,
+                        0);
                 }
             }
             if constexpr (LIST) {

@@ -61,6 +61,11 @@ hipError_t launch_stream_list(const StreamArgs &, int, hipStream_t)
     ++g_launches;
     return hipErrorInvalidValue;
 }
+hipError_t launch_stream_pooled(const StreamArgs &, int, hipStream_t)
+{
+    ++g_launches;
+    return hipErrorInvalidValue;
+}
 hipError_t launch_pool_queries(const void *, const float *, void *, float *, int64_t, int64_t,
                                int, int, int, int, hipStream_t)
 {
