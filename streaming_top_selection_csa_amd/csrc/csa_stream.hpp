@@ -986,6 +986,8 @@ stream_topk_kernel(StreamArgs a)
     constexpr int NDS = D / O::KSTEP;                // K steps per half tile
     constexpr int ROWB = D * O::ESZ;                 // LDS key row (swizzled, unpadded)
     constexpr int NC = ROWB / 16;                    // 16-byte chunks per key row
+    constexpr int RPL = ROWB >= 256 ? 1 : 256 / ROWB;  // key rows per 256-byte LDS line
+    auto swz = [](int r) { return (r / RPL) % NC; };
     constexpr int TILEB = KT * ROWB;
     constexpr int NDMA = TILEB / 1024;               // 1 KB wave DMA loads per tile
     constexpr int NDMA_W = (NDMA + kWaves - 1) / kWaves;
@@ -1165,9 +1167,11 @@ stream_topk_kernel(StreamArgs a)
 
         // ---- key tiles: direct global -> LDS loads into a ring of NBUF
         // buffers, NBUF-1 tiles ahead.  Row r of a tile keeps its 16-byte
-        // chunk c at chunk c ^ (r % NC), so the 32 lanes reading one chunk of
-        // 32 different rows hit distinct LDS banks; the swizzle is applied
-        // through each lane's source address.
+        // chunk c at chunk c ^ swz(r), swz(r) = (r / RPL) % NC with RPL rows
+        // per 256-byte line of the 64 LDS banks: the 16 lanes of a read
+        // cycle, one chunk of 16 consecutive rows, then fall on 16 distinct
+        // 16-byte bank groups.  The swizzle is applied through each lane's
+        // source address.
         const unsigned char *kbase = a.k + b * a.T * (D * O::ESZ);
         const float *ksbase = FP8 ? a.k_scale + b * a.T : nullptr;
         // DMA loads this wave issues per tile (the vmcnt it waits on); with
@@ -1198,7 +1202,7 @@ stream_topk_kernel(StreamArgs a)
                 if (j < NDMA) {
                     const int off = j * 1024 + lane * 16;  // LDS byte of this lane
                     const int r = off / ROWB;
-                    const int c = ((off % ROWB) / 16) ^ (r % NC);
+                    const int c = ((off % ROWB) / 16) ^ swz(r);
                     const unsigned char *src;
                     if constexpr (LIST) {
                         // a listed key row anywhere in k_cmp: 64-bit offset
@@ -1266,7 +1270,7 @@ stream_topk_kernel(StreamArgs a)
 #pragma unroll
             for (int ds = 0; ds < NDS; ++ds) {
                 const int c0 = (ds * O::KSTEP * O::ESZ + half * O::LANE_BYTES) / 16;
-                const OpT bk = O::load_swz(kb, c0, r % NC);
+                const OpT bk = O::load_swz(kb, c0, swz(r));
 #pragma unroll
                 for (int hb = 0; hb < 2; ++hb)
                     acc[hb] = O::mma(qa[hb][ds], bk, ds == 0 ? f32x16_t{} : acc[hb]);
