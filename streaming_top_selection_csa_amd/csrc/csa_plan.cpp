@@ -138,7 +138,9 @@ int make_plan(const csa_desc *desc, int32_t m, int32_t k,
     // rows of up to kMaxFusedSort slots are sorted at the end of the scoring
     // kernel (no key ranges); the others by a separate pass, which needs the
     // scores, in the workspace when the caller wants none
-    p.sort_e = (p.n_splits == 1 && p.sort_pow2 <= kMaxFusedSort) ? (p.sort_pow2 <= 512 ? 8 : 32) : 0;
+    p.sort_e = (p.n_splits == 1 && p.sort_pow2 <= kMaxFusedSort)
+                   ? (p.sort_pow2 <= 64 ? 1 : p.sort_pow2 <= 512 ? 8 : 32)
+                   : 0;
     // other key tiles exist for the sorted-row kernel only
     if (key_tile == 0) key_tile = p.sort_e > 0 ? default_key_tile(desc->H, desc->D) : kKeysPerTile;
     if (key_tile != kKeysPerTile &&

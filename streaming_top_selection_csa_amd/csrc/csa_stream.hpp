@@ -874,15 +874,20 @@ __device__ __forceinline__ void sort_store(uint32_t *su, uint32_t *si, int n, in
     }
 }
 
-// The final selection of one position's log and the sort of its row (rows
-// of up to 64*E keys).
-template <int NB, int E>
+// The final selection of one position's log and the sort of its row: rows
+// of up to 64*e keys, e = 1, 8 or 32 (one call site in the kernel).
+template <int NB>
 __device__ __noinline__ void final_sorted(uint32_t *lu, int32_t *li, int cnt, int k, uint32_t *h,
                                           int hbase, uint32_t *su, uint32_t *si, uint32_t *rhist,
-                                          int32_t *oi, float *os, int lane)
+                                          int32_t *oi, float *os, int e, int lane)
 {
     const int n = stage_select<NB>(lu, li, cnt, k, h, hbase, su, si, rhist, lane);
-    sort_store<E>(su, si, n, k, oi, os, lane);
+    if (e == 1)
+        sort_store<1>(su, si, n, k, oi, os, lane);
+    else if (e == 8)
+        sort_store<8>(su, si, n, k, oi, os, lane);
+    else
+        sort_store<32>(su, si, n, k, oi, os, lane);
 }
 
 // ------------------------------------------------------------ score epilogue
@@ -1401,14 +1406,9 @@ stream_topk_kernel(StreamArgs a)
                 const int64_t row = (b * a.S + pos) * a.topk;
                 int32_t *const oi = a.out_idx + row;
                 float *const os = a.out_score ? a.out_score + row : nullptr;
-                if (a.sort_e <= 8)
-                    final_sorted<NB, 8>(log_u + qi * a.log_cap, log_i + qi * a.log_cap, cnt[qi],
-                                        a.topk, &s_th[wave][qi * NB], hbase[qi], su, si, rhist,
-                                        oi, os, lane);
-                else
-                    final_sorted<NB, 32>(log_u + qi * a.log_cap, log_i + qi * a.log_cap, cnt[qi],
-                                         a.topk, &s_th[wave][qi * NB], hbase[qi], su, si, rhist,
-                                         oi, os, lane);
+                final_sorted<NB>(log_u + qi * a.log_cap, log_i + qi * a.log_cap, cnt[qi], a.topk,
+                                 &s_th[wave][qi * NB], hbase[qi], su, si, rhist, oi, os, a.sort_e,
+                                 lane);
             }
             continue;
         }
