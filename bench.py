@@ -40,7 +40,7 @@ if ROOT not in sys.path:
 METRIC = "indexer queries/sec + MFMA TFLOP/s (% peak) + peak HBM GB at S=262K, 1 GPU"
 PEAK_TFLOPS = {"bf16": 2500.0, "e4m3fn": 5000.0}   # MI355X dense MFMA
 KERNEL_SRC = os.path.join(ROOT, "streaming_top_selection_csa_amd", "csrc", "csa_stream.hpp")
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "stream_topk_s256k_pmc.md")
+PMC_DIR = os.path.join(ROOT, "profiles")
 ATTN_SRC = os.path.join(ROOT, "streaming_top_selection_csa_amd", "csrc", "csa_attn.hip")
 ATTN_PMC_SUMMARY = os.path.join(ROOT, "profiles", "sparse_attn_s256k_pmc.md")
 
@@ -68,10 +68,12 @@ def kernel_sha(src=KERNEL_SRC):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def traffic_from_profile(workload, summary=PMC_SUMMARY, src=KERNEL_SRC):
+def traffic_from_profile(workload, summary=None, src=KERNEL_SRC):
     """Bytes per launch beyond L2 (HBM and memory-side cache) from a
     committed counter summary, if it was taken on this kernel source and
-    workload."""
+    workload (profiles/stream_topk_<workload>_pmc.md by default)."""
+    if summary is None:
+        summary = os.path.join(PMC_DIR, "stream_topk_%s_pmc.md" % workload.replace("-", "_"))
     if not os.path.exists(summary):
         return None
     text = open(summary).read()
@@ -320,16 +322,23 @@ def sweep(csa, args):
 
 def grouped(csa, args):
     """The grouped (approximate) indexer on the S=65,536 workload: for each
-    group size and candidate count, the time of one call and the set recall
-    of its rows against the exact path (every row, csa_index) and against
-    the CPU oracle (256 sampled rows).  One JSON line per cell."""
+    query correlation rho (0: the i.i.d. gaussian workload; > 0: q rows of
+    one 64-position segment correlated with coefficient rho), group size and
+    candidate count, the time of one call and the set recall of its rows
+    against the exact path (every row, csa_index) and against the CPU
+    oracle (256 sampled rows).  One JSON line per cell."""
+    for rho in [float(r) for r in args.grouped_rho.split(",")]:
+        grouped_one(csa, args, rho)
+
+
+def grouped_one(csa, args, rho):
     import numpy as np
     import torch
 
     import oracle
     from csa_synth import WORKLOADS, make_inputs, sample_rows, storage_numpy
 
-    wl = WORKLOADS["s64k"]
+    wl = WORKLOADS["s64k"].with_(q_rho=rho)
     dev = torch.device("cuda:0")
     inp = make_inputs(wl, seed=0, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -377,7 +386,7 @@ def grouped(csa, args):
             r_or = recall(got[rows], o_idx)
             print(json.dumps({
                 "grouped": True, "workload": wl.name, "S": wl.S, "T": wl.n_keys, "k": wl.k,
-                "group": g, "candidates": C, "ms_per_step": ms, "call_ms": call_ms,
+                "q_rho": rho, "q_segment": wl.q_seg, "group": g, "candidates": C, "ms_per_step": ms, "call_ms": call_ms,
                 "queries_per_s": wl.S / (call_ms * 1e-3),
                 "exact_equivalent_tflops": flops_exact / (call_ms * 1e-3) / 1e12,
                 "recall_vs_exact_all_rows": {"mean": r_all[0], "min": r_all[1]},
@@ -408,6 +417,9 @@ def main():
     ap.add_argument("--grouped", action="store_true",
                     help="the grouped (approximate) indexer on the S=65,536 workload: time and "
                          "set recall for group sizes 8..64 and 2,048..8,192 candidates")
+    ap.add_argument("--grouped-rho", default="0,0.5,0.9",
+                    help="with --grouped: comma-separated correlations of q rows within "
+                         "64-position segments (0 = the i.i.d. workload)")
     ap.add_argument("--sweep-axes", default="",
                     help="with --sweep: comma-separated subset of chunk_keys,topk,key_tile,"
                          "range_keys")

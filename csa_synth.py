@@ -17,6 +17,12 @@ The distributions below are the ones the benchmark configurations name:
 * ``gauss`` : q ~ N(0, 1); k = (0.5 * (Z @ V) / sqrt(8) + E) / sqrt(D) with
               Z [T, 8], V [8, D], E [T, D] ~ N(0, 1) (a shared rank-8
               component plus noise); w = softplus(N(0, 1)).
+* ``gauss`` with ``q_rho`` > 0 (a sensitivity input for the grouped
+              indexer, not a benchmark configuration): q[t] =
+              sqrt(rho) * U[t // q_seg] + sqrt(1 - rho) * N(0, 1), with one
+              N(0, 1) row U per segment of q_seg consecutive positions, so
+              positions of one segment are correlated with coefficient rho
+              (every entry still N(0, 1)); k and w as ``gauss``.
 
 q and k are stored as bf16, or as OCP e4m3fn with one positive fp32 scale
 per row (per (t, head) row of q, per key of k): scale = amax / 448, values
@@ -47,6 +53,8 @@ class Workload:
     dtype: str = "bf16"     # "bf16" | "e4m3fn"
     T: int = -1             # -1: S // m
     row_offset: int = 0     # absolute position of q row 0
+    q_rho: float = 0.0      # gauss: correlation of q rows within a segment
+    q_seg: int = 64         # positions per segment (q_rho > 0)
 
     @property
     def n_keys(self) -> int:
@@ -136,7 +144,16 @@ def make_inputs(wl: Workload, seed: int = 0, device="cpu"):
         gw = _generator(device, seed, 10 * b + 2)
         gk = _generator(device, seed, 10 * b + 3)
 
-        def put_q(r0, r1, x, b=b):
+        useg = None
+        if wl.q_rho > 0 and not integer:
+            useg = _draw(((S + wl.q_seg - 1) // wl.q_seg, H, D), "normal",
+                         _generator(device, seed, 10 * b + 4), device)
+
+        def put_q(r0, r1, x, b=b, useg=useg):
+            if useg is not None:
+                seg = torch.arange(r0, r1, device=x.device) // wl.q_seg
+                x = (float(np.sqrt(1.0 - wl.q_rho)) * x +
+                     float(np.sqrt(wl.q_rho)) * useg.index_select(0, seg))
             if fp8 and not integer:
                 codes, sc = _fp8_rows(x)
                 q[b, r0:r1] = codes
