@@ -156,8 +156,9 @@ int run_index(const Plan &p, int cus, const void *q, const float *w, const void 
     a.out_idx = out_idx;
     // without a score output, a separate row sort keeps the scores in the workspace
     float *const scores = out_score ? out_score
-        : (p.sort_e == 0 ? reinterpret_cast<float *>(static_cast<unsigned char *>(ws) + p.score_offset)
-                         : nullptr);
+        : (p.sort_e == 0 && !p.merge_sorts
+               ? reinterpret_cast<float *>(static_cast<unsigned char *>(ws) + p.score_offset)
+               : nullptr);
     a.out_score = scores;
     a.ws = static_cast<uint32_t *>(ws);
     // unsorted lists: the ranges' partial lists, or with one range the output
@@ -205,7 +206,7 @@ int run_index(const Plan &p, int cus, const void *q, const float *w, const void 
     if (rc == CSA_OK &&
         launch_merge_splits(p, a.part_idx, a.part_score, out_idx, scores, cus, stream) != hipSuccess)
         rc = CSA_ERR_HIP;
-    if (rc == CSA_OK && p.sort_e == 0 &&
+    if (rc == CSA_OK && p.sort_e == 0 && !p.merge_sorts &&
         launch_sort_rows(p, out_idx, scores, cus, stream) != hipSuccess)
         rc = CSA_ERR_HIP;
     return rc;

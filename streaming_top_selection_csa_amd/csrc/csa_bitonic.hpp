@@ -81,4 +81,28 @@ __device__ __forceinline__ void bitonic_sort(unsigned long long (&key)[E], int l
     if constexpr (SIZE < 64 * E) bitonic_sort<E, SIZE * 2>(key, lane);
 }
 
+// Sorts pow2 64-bit keys in LDS ascending with a bitonic network run by the
+// nt threads of a workgroup (thread tid), one barrier per stage.  The
+// caller has made the keys visible (barrier) before the call; they are
+// visible to every thread on return.
+__device__ __forceinline__ void lds_bitonic_sort(unsigned long long *s_key, int pow2, int tid,
+                                                 int nt)
+{
+    for (int size = 2; size <= pow2; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = tid; i < pow2 / 2; i += nt) {
+                const int lo = ((i & ~(stride - 1)) << 1) | (i & (stride - 1));
+                const int hi = lo + stride;
+                const bool up = (lo & size) == 0;
+                const unsigned long long x = s_key[lo], y = s_key[hi];
+                if ((x > y) == up) {
+                    s_key[lo] = y;
+                    s_key[hi] = x;
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
 }  // namespace csa

@@ -4,6 +4,7 @@
 
 #include <cstdint>
 
+#include "csa_bitonic.hpp"
 #include "csa_stream.hpp"
 
 namespace csa {
@@ -97,12 +98,18 @@ __device__ __forceinline__ void digit_of_rank(const uint32_t *h, int need, uint3
 // 4 x 8-bit radix select over the lists takes its place.  Equal keys are
 // taken in list order.  Padding entries (index -1, score -inf) order below
 // every finite score and fill the row when fewer than k keys are visible.
+// SORTED (rows of next_pow2(k) = pow2 <= kMaxFusedSort slots): the chosen
+// entries go to LDS instead, as ascending 64-bit keys ~orderkey << 32 |
+// index, and the row leaves sorted by (score desc, key index asc); out_score
+// may then be null.
+template <bool SORTED>
 __global__ void __launch_bounds__(kMergeThreads)
 merge_splits_kernel(const int32_t *__restrict__ pidx, const float *__restrict__ pscore,
-                    int64_t rows, int G, int k, int32_t *__restrict__ out_idx,
+                    int64_t rows, int G, int k, int pow2, int32_t *__restrict__ out_idx,
                     float *__restrict__ out_score)
 {
     __shared__ MergeShared sh;
+    __shared__ unsigned long long s_row[SORTED ? kMaxFusedSort : 1];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -112,7 +119,16 @@ merge_splits_kernel(const int32_t *__restrict__ pidx, const float *__restrict__ 
         const int32_t *ri = pidx + row * n;
         const float *rs = pscore + row * n;
         int32_t *oi = out_idx + row * k;
-        float *os = out_score + row * k;
+        float *os = out_score ? out_score + row * k : nullptr;
+        // output slot p of the row: (index, score) with order key u
+        auto put = [&](int p, uint32_t u, int32_t idx, float sc) {
+            if constexpr (SORTED) {
+                s_row[p] = (static_cast<unsigned long long>(~u) << 32) | uint32_t(idx);
+            } else {
+                oi[p] = idx;
+                os[p] = sc;
+            }
+        };
 
         // ---- histogram of the top 12 bits
 #pragma unroll
@@ -200,10 +216,7 @@ merge_splits_kernel(const int32_t *__restrict__ pidx, const float *__restrict__ 
                     const uint32_t bin = u[j] >> 20;
                     if (valid && bin > bstar) {
                         const int p = atomicAdd(&sh.out, 1);
-                        if (p < n_above) {
-                            oi[p] = ri[e0 + j];
-                            os[p] = sc[j];
-                        }
+                        if (p < n_above) put(p, u[j], ri[e0 + j], sc[j]);
                     }
                     nc += (valid && bin == bstar) ? 1 : 0;
                 }
@@ -260,17 +273,11 @@ merge_splits_kernel(const int32_t *__restrict__ pidx, const float *__restrict__ 
                 const bool eq = i < in_bin && u == prefix;
                 if (gt) {
                     const int p = atomicAdd(&sh.out, 1);
-                    if (p < n_gt) {
-                        oi[p] = sh.ci[i];
-                        os[p] = key_to_float(u);
-                    }
+                    if (p < n_gt) put(p, u, sh.ci[i], key_to_float(u));
                 }
                 int tot;
                 const int r = eq_base + block_rank(eq, sh.w, lane, wave, &tot);
-                if (eq && r < need) {
-                    oi[n_gt + r] = sh.ci[i];
-                    os[n_gt + r] = key_to_float(u);
-                }
+                if (eq && r < need) put(n_gt + r, u, sh.ci[i], key_to_float(u));
                 eq_base += tot;
             }
         } else {
@@ -309,21 +316,27 @@ merge_splits_kernel(const int32_t *__restrict__ pidx, const float *__restrict__ 
                 const bool eq = e < n && u == prefix;
                 if (gt) {
                     const int p = atomicAdd(&sh.out, 1);
-                    if (p < n_gt) {
-                        oi[p] = ri[e];
-                        os[p] = sc;
-                    }
+                    if (p < n_gt) put(p, u, ri[e], sc);
                 }
                 int tot;
                 const int r = eq_base + block_rank(eq, sh.w, lane, wave, &tot);
-                if (eq && r < need) {
-                    oi[n_gt + r] = ri[e];
-                    os[n_gt + r] = sc;
-                }
+                if (eq && r < need) put(n_gt + r, u, ri[e], sc);
                 eq_base += tot;
             }
         }
         __syncthreads();
+        if constexpr (SORTED) {
+            // the k chosen entries, padding slots after them, sorted in LDS
+            for (int e = k + tid; e < pow2; e += kMergeThreads) s_row[e] = ~0ull;
+            __syncthreads();
+            lds_bitonic_sort(s_row, pow2, tid, kMergeThreads);
+            for (int e = tid; e < k; e += kMergeThreads) {
+                const unsigned long long key = s_row[e];
+                oi[e] = int32_t(uint32_t(key));
+                if (os) os[e] = key_to_float(~uint32_t(key >> 32));
+            }
+            __syncthreads();
+        }
     }
 }
 
@@ -334,8 +347,14 @@ hipError_t launch_merge_splits(const Plan &p, const int32_t *part_idx, const flo
     if (rows <= 0 || p.n_splits <= 1) return hipSuccess;
     const int64_t cap = int64_t(num_cus) * 4;
     const int grid = int(rows < cap ? rows : cap);
-    hipLaunchKernelGGL(merge_splits_kernel, dim3(grid), dim3(kMergeThreads), 0, s, part_idx,
-                       part_score, rows, p.n_splits, p.k, out_idx, out_score);
+    if (p.merge_sorts)
+        hipLaunchKernelGGL(merge_splits_kernel<true>, dim3(grid), dim3(kMergeThreads), 0, s,
+                           part_idx, part_score, rows, p.n_splits, p.k, p.sort_pow2, out_idx,
+                           out_score);
+    else
+        hipLaunchKernelGGL(merge_splits_kernel<false>, dim3(grid), dim3(kMergeThreads), 0, s,
+                           part_idx, part_score, rows, p.n_splits, p.k, p.sort_pow2, out_idx,
+                           out_score);
     return hipGetLastError();
 }
 

@@ -141,6 +141,9 @@ int make_plan(const csa_desc *desc, int32_t m, int32_t k,
     p.sort_e = (p.n_splits == 1 && p.sort_pow2 <= kMaxFusedSort)
                    ? (p.sort_pow2 <= 64 ? 1 : p.sort_pow2 <= 512 ? 8 : 32)
                    : 0;
+    // with key ranges and fewer rows than compute units (short query blocks)
+    // the merge kernel, one workgroup per row, also sorts the row
+    p.merge_sorts = p.n_splits > 1 && p.sort_pow2 <= kMaxFusedSort && rows < resident;
     // other key tiles exist for the sorted-row kernel only
     if (key_tile == 0) key_tile = p.sort_e > 0 ? default_key_tile(desc->H, desc->D) : kKeysPerTile;
     if (key_tile != kKeysPerTile &&
@@ -154,7 +157,8 @@ int make_plan(const csa_desc *desc, int32_t m, int32_t k,
     p.part_offset = logs;
     const size_t parts = p.n_splits > 1 ? size_t(rows) * size_t(p.n_splits) * size_t(k) * 8u : 0u;
     p.score_offset = logs + (parts + 255) / 256 * 256;
-    const size_t scores = (no_score && p.sort_e == 0) ? size_t(rows) * size_t(k) * 4u : 0u;
+    const size_t scores =
+        (no_score && p.sort_e == 0 && !p.merge_sorts) ? size_t(rows) * size_t(k) * 4u : 0u;
     p.ws_bytes = p.score_offset + (scores + 255) / 256 * 256;
     *plan = p;
     return CSA_OK;

@@ -53,6 +53,7 @@ struct Plan {
     int log_cap = 0;            // k + chunk
     int sort_pow2 = 0;          // next power of two >= k
     int sort_e = 0;             // > 0: the scoring kernel sorts the rows (sort_e keys per lane)
+    bool merge_sorts = false;   // key ranges, few rows: the merge kernel sorts the rows
     int key_tile = kKeysPerTile;  // keys staged in LDS per workgroup step
     bool no_score = false;      // the caller passes no score output
     int64_t pos_mul = 1;        // q row i is position row_offset + i * pos_mul

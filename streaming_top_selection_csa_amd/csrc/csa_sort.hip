@@ -37,21 +37,7 @@ sort_rows_kernel(int32_t *out_idx, float *out_score, int64_t nrows, int k, int p
             s_key[e] = key;
         }
         __syncthreads();
-        for (int size = 2; size <= pow2; size <<= 1) {
-            for (int stride = size >> 1; stride > 0; stride >>= 1) {
-                for (int i = tid; i < pow2 / 2; i += NT) {
-                    const int lo = ((i & ~(stride - 1)) << 1) | (i & (stride - 1));
-                    const int hi = lo + stride;
-                    const bool up = (lo & size) == 0;
-                    const unsigned long long x = s_key[lo], y = s_key[hi];
-                    if ((x > y) == up) {
-                        s_key[lo] = y;
-                        s_key[hi] = x;
-                    }
-                }
-                __syncthreads();
-            }
-        }
+        lds_bitonic_sort(s_key, pow2, tid, NT);
         for (int e = tid; e < k; e += NT) {
             const unsigned long long key = s_key[e];
             ri[e] = int32_t(uint32_t(key));

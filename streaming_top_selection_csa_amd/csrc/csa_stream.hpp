@@ -9,18 +9,20 @@
 // Here that is one persistent kernel:
 //
 //   stream_topk_kernel  Each wave owns 64 (position, head) rows of q, held in
-//       VGPRs as MFMA A-operands.  The workgroup stages 64-key tiles of k_cmp
-//       in LDS (a ring of three, two tiles ahead).  Per tile a wave runs the
-//       [64 rows x D] x [D x 64 keys] contraction on the matrix cores (bf16
-//       32x32x16 or fp8 32x32x64), then in registers applies ReLU, the
-//       per-head weights and the head sum, and the causal cut.  A score
+//       VGPRs as MFMA A-operands.  The workgroup stages tiles of KT keys of
+//       k_cmp in LDS (64 or 128 keys; a ring of three, two tiles ahead, or
+//       of two).  Per 64 keys a wave runs the [64 rows x D] x [D x 64 keys]
+//       contraction on the matrix cores (bf16 32x32x16 or fp8 32x32x64),
+//       then in registers applies ReLU, the per-head weights and the head
+//       sum, and the causal cut.  A score
 //       survives only if it beats the position's running threshold, which a
 //       per-position histogram of the candidates raises to just below the
 //       k-th best so far; survivors are appended, in key order, to the
 //       position's candidate log.  A full log (k + chunk entries) is
 //       compacted to the entries above the threshold (the merge step, with an
 //       exact radix select as the fallback).  At the end the histogram and
-//       one pass over the log give the exact top-min(k, n_vis) set.
+//       one pass over the log give the exact top-min(k, n_vis) set, which is
+//       sorted in registers and written to the output row.
 //
 // With key ranges (SPLIT) a unit is one (query block, key range) pair and
 // the kernel leaves the exact top-k of the range in a partial list; the merge
@@ -1280,15 +1282,15 @@ stream_topk_kernel(StreamArgs a)
                 for (int hb = 0; hb < 2; ++hb)
                     acc[hb] = O::mma(qa[hb][ds], bk, ds == 0 ? f32x16_t{} : acc[hb]);
             }
-            // operand reads one K step ahead of their MFMAs
+            // operand reads two K steps ahead of their MFMAs
             constexpr int RD = FP8 ? 2 : 1;  // LDS reads per K step
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * RD, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 3 * RD, 0);
 #pragma unroll
-            for (int st = 0; st < NDS - 2; ++st) {
+            for (int st = 0; st < NDS - 3; ++st) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
         };
         // scores of compute tile it from the two half partials; filter and append
         auto finish = [&](const float (&ha)[E::NP], const float (&hb)[E::NP], int it, float ksv) {

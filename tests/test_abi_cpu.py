@@ -369,7 +369,8 @@ def test_host_code_fuzz_under_sanitizers(tmp_path):
 def test_no_score_workspace_sizes(lib):
     """CSA_FLAG_NO_SCORE sizes the workspace for out_score = NULL: nothing
     extra when the scoring kernel sorts the rows (next_pow2(k) <= 2048, no
-    key ranges), B*S*k*4 more bytes when a separate pass sorts them."""
+    key ranges) or the merge kernel does (key ranges, fewer rows than
+    compute units), B*S*k*4 more bytes when a separate pass sorts them."""
     d = csa.make_desc(1, 100000, 25000, 64, 128)
     ns = opts(flags=csa.CSA_FLAG_NO_SCORE)
     assert csa.workspace_bytes(d, 4, 2048, ns) == csa.workspace_bytes(d, 4, 2048, opts())
@@ -378,8 +379,12 @@ def test_no_score_workspace_sizes(lib):
     few = csa.make_desc(1, 64, 65536, 64, 128)
     o = opts(row_offset=262080, key_splits=8)
     o_ns = opts(row_offset=262080, key_splits=8, flags=csa.CSA_FLAG_NO_SCORE)
-    assert csa.workspace_bytes(few, 4, 2048, o_ns) - csa.workspace_bytes(few, 4, 2048, o) == \
-        64 * 2048 * 4
+    assert csa.workspace_bytes(few, 4, 2048, o_ns) == csa.workspace_bytes(few, 4, 2048, o)
+    many = csa.make_desc(1, 4096, 16384, 64, 128)
+    o = opts(key_splits=4)
+    o_ns = opts(key_splits=4, flags=csa.CSA_FLAG_NO_SCORE)
+    assert csa.workspace_bytes(many, 4, 2048, o_ns) - csa.workspace_bytes(many, 4, 2048, o) == \
+        4096 * 2048 * 4
     # other flag bits are invalid
     assert csa.workspace_bytes(d, 4, 2048, opts(flags=2)) == 0
 

@@ -42,7 +42,8 @@ CASES = [
     (1, 3000, 4, 64, 128, 512, -1, 0, 0),      # sorted in the kernel, 8 keys per lane
     (1, 3000, 4, 64, 128, 2048, -1, 0, 0),     # sorted in the kernel, 32 keys per lane
     (2, 700, 2, 8, 64, 100, -1, 0, 0),         # several positions per wave
-    (1, 64, 4, 64, 128, 512, 4096, 16320, 0),  # key ranges: separate sort, scores in workspace
+    (1, 64, 4, 64, 128, 512, 4096, 16320, 0),  # key ranges, few rows: the merge kernel sorts
+    (1, 3000, 4, 64, 128, 512, -1, 0, 4),      # key ranges, many rows: separate sort, scores in workspace
     (1, 900, 1, 16, 32, 3000, -1, 0, 0),       # k > 2048: separate sort, scores in workspace
 ]
 
