@@ -34,6 +34,7 @@
 
 #include <cstdint>
 
+#include "csa_dma.hpp"
 #include "csa_kernels.hpp"
 
 namespace csa {
@@ -170,8 +171,7 @@ sparse_attn_kernel(AttnArgs a, int64_t unit0, int64_t nunits)
             const int swz = is_v ? (2 * r) % NC : r % NC;
             const unsigned char *src = (is_v ? vbase : kbase) +
                                        int64_t(s >= 0 ? s : 0) * ROWB + 16 * (p ^ swz);
-            __builtin_amdgcn_global_load_lds(
-                src, (__attribute__((address_space(3))) void *)&s_ring[buf][j * 1024], 16, 0, 0);
+            dma16(src, &s_ring[buf][j * 1024]);
         }
     };
 
