@@ -1294,6 +1294,44 @@ stream_topk_kernel(StreamArgs a)
             }
             __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
         };
+        // fp8: the operands of a half's first two K steps are read earlier
+        // (mma_pre), before the vector work that precedes the half, so that
+        // its first MFMAs do not wait on LDS (bf16: no gain, more spills)
+        constexpr bool PF = FP8;
+        OpT bpf[2];
+        auto mma_pre = [&](int buf, int r0) {
+            if constexpr (PF) {
+                const int r = r0 + col;
+                const unsigned char *kb = &s_k[buf][r * ROWB];
+#pragma unroll
+                for (int ds = 0; ds < 2; ++ds)
+                    bpf[ds] = O::load_swz(kb, (ds * O::KSTEP * O::ESZ + half * O::LANE_BYTES) / 16, swz(r));
+            }
+        };
+        auto mma_half_pf = [&](int buf, int r0) {
+            if constexpr (!PF) {
+                mma_half(buf, r0);
+            } else {
+                const int r = r0 + col;
+                const unsigned char *kb = &s_k[buf][r * ROWB];
+#pragma unroll
+                for (int ds = 0; ds < NDS; ++ds) {
+                    const int c0 = (ds * O::KSTEP * O::ESZ + half * O::LANE_BYTES) / 16;
+                    const OpT bk = ds < 2 ? bpf[ds] : O::load_swz(kb, c0, swz(r));
+#pragma unroll
+                    for (int hb = 0; hb < 2; ++hb)
+                        acc[hb] = O::mma(qa[hb][ds], bk, ds == 0 ? f32x16_t{} : acc[hb]);
+                }
+                constexpr int RD = 2;  // LDS reads per K step
+                __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+#pragma unroll
+                for (int st = 0; st < NDS - 3; ++st) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+            }
+        };
         // scores of compute tile it from the two half partials; filter and append
         auto finish = [&](const float (&ha)[E::NP], const float (&hb)[E::NP], int it, float ksv) {
             float sc[QW];
@@ -1370,23 +1408,26 @@ stream_topk_kernel(StreamArgs a)
             } else {
                 if (!lagging) {
                     mma_half(buf, r0);
+                    mma_pre(buf, r0 + 32);
                     E::partial(acc, wr, h0);
                     __builtin_amdgcn_sched_barrier(0);
-                    mma_half(buf, r0 + 32);
+                    mma_half_pf(buf, r0 + 32);
                     E::partial(acc, wr, h1);
                     finish(h0, h1, it, ksv);
                     if (stage) dma_tile(st + PD, (st + PD) % NBUF);
                 } else {
+                    mma_pre(buf, r0);
                     if (it > 0) {
                         E::partial(acc, wr, h1);
                         __builtin_amdgcn_sched_barrier(0);
                         finish(h0, h1, it - 1, ksv_prev);
                     }
                     if (stage) dma_tile(st + PD, (st + PD) % NBUF);
-                    mma_half(buf, r0);
+                    mma_half_pf(buf, r0);
+                    mma_pre(buf, r0 + 32);
                     E::partial(acc, wr, h0);
                     __builtin_amdgcn_sched_barrier(0);
-                    mma_half(buf, r0 + 32);
+                    mma_half_pf(buf, r0 + 32);
                 }
                 ksv_prev = ksv;
                 if (last) sync_tiles(later_loads(st, nst));
