@@ -19,15 +19,18 @@ bool key_tile_supported(int key_tile, int dtype, int H, int D)
 {
     if (key_tile == kKeysPerTile) return true;
     if (H != 64 || D != 128) return false;
-    if (dtype == CSA_FP8_E4M3FN) return key_tile == 128;
+    if (dtype == CSA_FP8_E4M3FN) return key_tile == 128 || key_tile == 256;
     return key_tile == 32 || key_tile == 128 || key_tile == 192 || key_tile == 256;
 }
 
-int default_key_tile(int H, int D)
+int default_key_tile(int H, int D, int dtype)
 {
-    // two 64-key compute tiles per staged tile halve the workgroup barriers
-    // (measured faster at H_I = 64, d_I = 128)
-    return H == 64 && D == 128 ? 128 : kKeysPerTile;
+    // several 64-key compute tiles per staged tile cut the workgroup
+    // barriers (measured faster at H_I = 64, d_I = 128: two for bf16, whose
+    // larger tiles spill or leave room for only two buffers; four for fp8,
+    // whose 128-byte rows still fit a ring of three)
+    if (H != 64 || D != 128) return kKeysPerTile;
+    return dtype == CSA_FP8_E4M3FN ? 256 : 128;
 }
 
 static int64_t next_pow2(int64_t x)
@@ -145,7 +148,7 @@ int make_plan(const csa_desc *desc, int32_t m, int32_t k,
     // the merge kernel, one workgroup per row, also sorts the row
     p.merge_sorts = p.n_splits > 1 && p.sort_pow2 <= kMaxFusedSort && rows < resident;
     // other key tiles exist for the sorted-row kernel only
-    if (key_tile == 0) key_tile = p.sort_e > 0 ? default_key_tile(desc->H, desc->D) : kKeysPerTile;
+    if (key_tile == 0) key_tile = p.sort_e > 0 ? default_key_tile(desc->H, desc->D, desc->dtype) : kKeysPerTile;
     if (key_tile != kKeysPerTile &&
         (!key_tile_supported(key_tile, desc->dtype, desc->H, desc->D) || p.sort_e == 0))
         return CSA_ERR_UNSUPPORTED;

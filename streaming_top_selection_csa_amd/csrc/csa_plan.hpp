@@ -66,7 +66,7 @@ bool supported(int dtype, int H, int D);
 // Staged key tiles other than kKeysPerTile are built for H = 64, D = 128
 // only (bf16: 32, 128, 192, 256; fp8: 128); the default there is 128.
 bool key_tile_supported(int key_tile, int dtype, int H, int D);
-int default_key_tile(int H, int D);
+int default_key_tile(int H, int D, int dtype);
 
 // Validates every argument and fills `plan`.  num_cus must be > 0.
 // no_score: the call writes no scores (also implied by CSA_FLAG_NO_SCORE).

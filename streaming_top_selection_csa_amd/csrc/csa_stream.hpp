@@ -55,6 +55,15 @@ __device__ __forceinline__ float relu(float x)
     return __int_as_float(b > 0 ? b : 0);
 }
 
+// The smallest score whose order key exceeds tau, so that for a finite
+// score x, order_key(x) > tau <=> x >= score_floor(tau).  Keys below that of
+// -inf (tau + 1 has no float) give -inf: every finite score passes.  Should
+// the compare flush denormals, it can only let extra scores pass.
+__device__ __forceinline__ float score_floor(uint32_t tau)
+{
+    return tau < 0x007FFFFFu ? -__builtin_huge_valf() : key_to_float(tau + 1u);
+}
+
 // Number of set bits of `m` in lanes below this lane.
 __device__ __forceinline__ int lanes_below(uint64_t m)
 {
@@ -1091,6 +1100,11 @@ stream_topk_kernel(StreamArgs a)
         }
         int nv[QW];
         uint32_t tau[QW];   // a later key at or below tau is beaten by k earlier keys
+        // fp8 takes the same test on the score, order key > tau <=> score >=
+        // tauf, and orders only the scores of tiles where some lane passes
+        // (measured faster with fp8's 256-key tiles; slower for bf16)
+        constexpr bool SCORE_TEST = FP8;
+        float tauf[QW];
         int cnt[QW];        // log entries
         int pend[QW];       // appends since the last threshold refresh
         int hbase[QW];      // global bin of threshold-histogram bin 0
@@ -1100,6 +1114,7 @@ stream_topk_kernel(StreamArgs a)
             nv[qi] = pos < a.S ? int(n_visible(position(pos), a.T, a.m)) : 0;
             if (SPLIT && nv[qi] > n_hi) nv[qi] = n_hi;  // the end of the key range
             tau[qi] = 0u;  // below the key of any finite score: accept all
+            if constexpr (SCORE_TEST) tauf[qi] = score_floor(0u);
             cnt[qi] = 0;
             pend[qi] = 0;
             hbase[qi] = 0;
@@ -1116,10 +1131,11 @@ stream_topk_kernel(StreamArgs a)
             for (int qi = 0; qi < QW; ++qi) {
                 const int r = qi;
                 if (!LIST && kt >= nv[qi]) continue;  // wave-uniform
-                const uint32_t u = order_key(sc[r]);
-                const bool pass = key < nv[qi] && u > tau[qi];
+                uint32_t u = SCORE_TEST ? 0u : order_key(sc[r]);
+                const bool pass = key < nv[qi] && (SCORE_TEST ? sc[r] >= tauf[qi] : u > tau[qi]);
                 const uint64_t mk = __ballot(pass);
                 if (mk == 0) continue;
+                if constexpr (SCORE_TEST) u = order_key(sc[r]);
                 uint32_t *h = &s_th[wave][qi * NB];
                 const int gb = int(u >> 16);
                 if (cnt[qi] == 0) {
@@ -1151,7 +1167,10 @@ stream_topk_kernel(StreamArgs a)
                     const int gstar = hbase[qi] + bstar;
                     if (bstar > 0 && gstar > 0) {
                         const uint32_t t2 = (uint32_t(gstar) << 16) - 1u;
-                        if (t2 > tau[qi]) tau[qi] = t2;
+                        if (t2 > tau[qi]) {
+                            tau[qi] = t2;
+                            if constexpr (SCORE_TEST) tauf[qi] = score_floor(t2);
+                        }
                         Hist<NB>::zero_below(h, bstar, lane);
                     }
                     pend[qi] = 0;
@@ -1166,6 +1185,7 @@ stream_topk_kernel(StreamArgs a)
                     if (cnt[qi] > (room < a.log_cap - CT ? room : a.log_cap - CT)) {
                         // the bins could not separate enough: exact merge
                         tau[qi] = __builtin_amdgcn_readfirstlane(merge_log(lu, li, cnt[qi], a.topk, rhist, lane));
+                        if constexpr (SCORE_TEST) tauf[qi] = score_floor(tau[qi]);
                         cnt[qi] = a.topk;
                         hist_recount<NB>(h, hbase[qi], lu, cnt[qi], lane);
                     }
@@ -1487,6 +1507,11 @@ static hipError_t launch_one(const StreamArgs &a, int grid, hipStream_t s)
     if constexpr (H == 64 && D == 128 && FP8) {
         if (a.key_tile == 128) {
             hipLaunchKernelGGL((stream_topk_kernel<H, D, FP8, false, 128>), dim3(grid),
+                               dim3(kThreads), 0, s, a);
+            return hipGetLastError();
+        }
+        if (a.key_tile == 256) {
+            hipLaunchKernelGGL((stream_topk_kernel<H, D, FP8, false, 256>), dim3(grid),
                                dim3(kThreads), 0, s, a);
             return hipGetLastError();
         }

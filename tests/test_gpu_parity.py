@@ -108,6 +108,16 @@ def test_fp8_integer_exact(csa):
     _check(csa, wl, seed=5)
 
 
+@pytest.mark.parametrize("key_tile", [64, 128, 256])
+def test_fp8_key_tiles_integer_exact(csa, key_tile):
+    """Every staged key tile of the fp8 kernel (256 is its default), on
+    integer inputs whose key count is no multiple of any tile, every row
+    exact."""
+    wl = Workload("fp8-tiles", B=2, S=3001, m=4, H=64, D=128, k=300, dist="int",
+                  dtype="e4m3fn", T=700)
+    _check(csa, wl, seed=11, key_tile=key_tile)
+
+
 def test_fp8_gauss_all_rows(csa):
     wl = Workload("fp8g", B=1, S=2048, m=4, H=64, D=128, k=128, dtype="e4m3fn")
     _, _, stats = _check(csa, wl, seed=6)
