@@ -16,18 +16,20 @@ namespace csa {
 // that stay in registers: DPP quad permutes (1, 2), a bit-mask swizzle
 // inside each half-wave (4), a DPP rotation by half a 16-lane row (8), and
 // the row-pair and half-wave swaps (16, 32), which give every lane both the
-// lower and the upper lane's value.
+// lower and the upper lane's value.  The DPP forms are full permutations
+// with every row and bank enabled, so no lane keeps its old value: the moves
+// take none (an `old` operand would cost a register initialisation each).
 template <int D>
 __device__ __forceinline__ uint32_t lane_xor(uint32_t v, int lane)
 {
     if constexpr (D == 1) {
-        return __builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xf, 0xf, false);  // quad_perm 1,0,3,2
+        return uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0xB1, 0xf, 0xf, false));  // quad_perm 1,0,3,2
     } else if constexpr (D == 2) {
-        return __builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xf, 0xf, false);  // quad_perm 2,3,0,1
+        return uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0x4E, 0xf, 0xf, false));  // quad_perm 2,3,0,1
     } else if constexpr (D == 4) {
         return uint32_t(__builtin_amdgcn_ds_swizzle(int(v), 0x101F));      // and 31, xor 4
     } else if constexpr (D == 8) {
-        return __builtin_amdgcn_update_dpp(0u, v, 0x128, 0xf, 0xf, false); // row_ror:8
+        return uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0x128, 0xf, 0xf, false));  // row_ror:8
     } else if constexpr (D == 16) {
         const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
         return (lane & 16) ? r[0] : r[1];
