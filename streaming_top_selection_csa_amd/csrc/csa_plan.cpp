@@ -136,7 +136,9 @@ int make_plan(const csa_desc *desc, int32_t m, int32_t k,
     p.n_units = p.n_blocks * p.n_splits;
     p.grid = int(p.n_units < resident ? p.n_units : resident);
     p.chunk = chunk;
-    p.log_cap = k + chunk;
+    // rounded up so that the final selection can read whole groups of
+    // entries with 16-byte loads
+    p.log_cap = int((int64_t(k) + chunk + kLogCapMultiple - 1) / kLogCapMultiple * kLogCapMultiple);
     p.sort_pow2 = int(next_pow2(k));
     // rows of up to kMaxFusedSort slots are sorted at the end of the scoring
     // kernel (no key ranges); the others by a separate pass, which needs the

@@ -33,6 +33,7 @@ constexpr int kKeysPerTile = 64;    // compressed keys per compute tile (one key
 constexpr int kMaxTopK = 16384;     // row sort holds next_pow2(k) keys in LDS
 constexpr int kMaxFusedSort = 2048; // rows up to this next_pow2(k) are sorted by the scoring kernel
 constexpr int kMaxChunk = 1 << 20;
+constexpr int kLogCapMultiple = 8;  // candidate-log capacity granularity (entries)
 constexpr int64_t kMaxKeys = int64_t(1) << 30;   // largest T
 constexpr int kMinSplitKeys = 1024;              // smallest automatic key range
 constexpr size_t kMaxSplitBytes = size_t(1) << 30;  // bound of the partial lists (automatic G)

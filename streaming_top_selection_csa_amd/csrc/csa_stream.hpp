@@ -190,6 +190,9 @@ struct Op<true> {
 // ------------------------------------------------------- candidate merging
 
 constexpr int kBatch = 8;  // log entries per lane in flight in the log passes
+// Consecutive log entries one lane reads in the final staging pass; the
+// planner keeps every log's capacity a multiple of it.
+constexpr int kLogGroup = kLogCapMultiple;
 
 // The log lu/li[0..n) holds candidates of one position in ascending key
 // order, n > k.  Finds the k-th best under (score desc, key asc) with a
@@ -727,30 +730,54 @@ __device__ __forceinline__ int stage_select(uint32_t *lu, int32_t *li, int cnt, 
         uint32_t *const cu = h;
         int32_t *const ci = reinterpret_cast<int32_t *>(h + CAP);
         int wpos = 0, cpos = 0;
+        // Each lane takes kLogGroup consecutive entries with two 16-byte
+        // loads per array (the log's capacity is a multiple of kLogGroup, so
+        // a group that starts below cnt lies inside it).  Ranks come from
+        // the lanes' counts and one prefix sum per kind, so the entries
+        // keep their log order.
 #pragma unroll 1
-        for (int base = 0; base < cnt; base += 64 * kBatch) {
-            uint32_t u[kBatch];
-            int32_t id[kBatch];
+        for (int base = 0; base < cnt; base += 64 * kLogGroup) {
+            const int e0 = base + lane * kLogGroup;
+            uint32_t u[kLogGroup];
+            int32_t id[kLogGroup];
+            if (e0 < cnt) {
+                const uint4 *pu = reinterpret_cast<const uint4 *>(lu + e0);
+                const int4 *pi = reinterpret_cast<const int4 *>(li + e0);
 #pragma unroll
-            for (int j = 0; j < kBatch; ++j) {
-                const int e = base + 64 * j + lane;
-                u[j] = e < cnt ? lu[e] : 0u;
-                id[j] = e < cnt ? li[e] : 0;
-            }
-#pragma unroll
-            for (int j = 0; j < kBatch; ++j) {
-                const bool valid = base + 64 * j + lane < cnt;
-                const bool sel = valid && u[j] >= hi;
-                const bool cand = valid && u[j] >= lo && u[j] < hi;
-                const uint64_t ms = __ballot(sel);
-                const uint64_t mc = __ballot(cand);
-                const int ps = wpos + lanes_below(ms);
-                const int pc = cpos + lanes_below(mc);
-                if (sel && ps < k) {
-                    su[stage_word(ps)] = u[j];
-                    si[stage_word(ps)] = uint32_t(id[j]);
+                for (int v = 0; v < kLogGroup / 4; ++v) {
+                    const uint4 x = pu[v];
+                    const int4 y = pi[v];
+                    u[4 * v] = x.x, u[4 * v + 1] = x.y, u[4 * v + 2] = x.z, u[4 * v + 3] = x.w;
+                    id[4 * v] = y.x, id[4 * v + 1] = y.y, id[4 * v + 2] = y.z, id[4 * v + 3] = y.w;
                 }
-                if (cand) {
+            } else {
+#pragma unroll
+                for (int j = 0; j < kLogGroup; ++j) u[j] = 0u, id[j] = 0;
+            }
+            bool sel[kLogGroup], cand[kLogGroup];
+            uint32_t ns = 0u, nc = 0u;
+#pragma unroll
+            for (int j = 0; j < kLogGroup; ++j) {
+                const bool valid = e0 + j < cnt;
+                sel[j] = valid && u[j] >= hi;
+                cand[j] = valid && u[j] >= lo && u[j] < hi;
+                ns += sel[j] ? 1u : 0u;
+                nc += cand[j] ? 1u : 0u;
+            }
+            const uint32_t is = wave_prefix_sum(ns);
+            const uint32_t ic = wave_prefix_sum(nc);
+            int ps = wpos + int(is - ns);
+            int pc = cpos + int(ic - nc);
+#pragma unroll
+            for (int j = 0; j < kLogGroup; ++j) {
+                if (sel[j]) {
+                    if (ps < k) {
+                        su[stage_word(ps)] = u[j];
+                        si[stage_word(ps)] = uint32_t(id[j]);
+                    }
+                    ++ps;
+                }
+                if (cand[j]) {
                     if (direct) {
                         if (pc < need) {
                             su[stage_word(int(above) + pc)] = u[j];
@@ -760,10 +787,11 @@ __device__ __forceinline__ int stage_select(uint32_t *lu, int32_t *li, int cnt, 
                         cu[pc] = u[j];
                         ci[pc] = id[j];
                     }
+                    ++pc;
                 }
-                wpos += __popcll(ms);
-                cpos += __popcll(mc);
             }
+            wpos += int(__builtin_amdgcn_readlane(is, 63));
+            cpos += int(__builtin_amdgcn_readlane(ic, 63));
         }
         wave_lds_sync();
         if (wpos == int(above) && cpos == int(nb)) {
