@@ -16,6 +16,12 @@ constexpr int kMergeWaves = kMergeThreads / 64;
 constexpr int kMergeBins = 4096;  // top 12 bits of the order key
 constexpr int kMergeCap = 6144;   // candidates of the k-th bin held in LDS
 constexpr int kMergeEpt = 8;      // consecutive list entries per thread in the gather
+// With 16-byte loads (k a multiple of 4, lists 16-byte aligned) each thread
+// takes more entries per step, so that a row's passes need fewer dependent
+// round trips to memory: the lists of short query blocks come from other
+// XCDs and miss L2.
+constexpr int kMergeHistV = 16;   // entries per thread per histogram step
+constexpr int kMergeEptV = 16;    // entries per thread per gather step
 
 struct MergeShared {
     uint32_t hist[kMergeBins];
@@ -102,7 +108,7 @@ __device__ __forceinline__ void digit_of_rank(const uint32_t *h, int need, uint3
 // entries go to LDS instead, as ascending 64-bit keys ~orderkey << 32 |
 // index, and the row leaves sorted by (score desc, key index asc); out_score
 // may then be null.
-template <bool SORTED>
+template <bool SORTED, bool VEC>
 __global__ void __launch_bounds__(kMergeThreads)
 merge_splits_kernel(const int32_t *__restrict__ pidx, const float *__restrict__ pscore,
                     int64_t rows, int G, int k, int pow2, int32_t *__restrict__ out_idx,
@@ -138,15 +144,35 @@ merge_splits_kernel(const int32_t *__restrict__ pidx, const float *__restrict__ 
             sh.out = 0;
         }
         __syncthreads();
-        for (int base = 0; base < n; base += 4 * kMergeThreads) {
-            uint32_t bin[4];
+        constexpr int HB = VEC ? kMergeHistV : 4;  // entries per thread per step
+        for (int base = 0; base < n; base += HB * kMergeThreads) {
+            uint32_t bin[HB];
+            if constexpr (VEC) {
+                // thread t reads entries [base + t*HB, base + (t+1)*HB); n is
+                // a multiple of 4, so a group of 4 lies wholly inside or out
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int e = base + j * kMergeThreads + tid;
-                bin[j] = e < n ? order_key(rs[e]) >> 20 : uint32_t(kMergeBins);
+                for (int q = 0; q < HB / 4; ++q) {
+                    const int e = base + tid * HB + 4 * q;
+                    if (e < n) {
+                        const float4 v = *reinterpret_cast<const float4 *>(rs + e);
+                        bin[4 * q] = order_key(v.x) >> 20;
+                        bin[4 * q + 1] = order_key(v.y) >> 20;
+                        bin[4 * q + 2] = order_key(v.z) >> 20;
+                        bin[4 * q + 3] = order_key(v.w) >> 20;
+                    } else {
+                        bin[4 * q] = bin[4 * q + 1] = bin[4 * q + 2] = bin[4 * q + 3] =
+                            uint32_t(kMergeBins);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < HB; ++j) {
+                    const int e = base + j * kMergeThreads + tid;
+                    bin[j] = e < n ? order_key(rs[e]) >> 20 : uint32_t(kMergeBins);
+                }
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < HB; ++j)
                 if (bin[j] < uint32_t(kMergeBins)) atomicAdd(&sh.hist[bin[j]], 1u);
         }
         __syncthreads();
@@ -197,26 +223,51 @@ merge_splits_kernel(const int32_t *__restrict__ pidx, const float *__restrict__ 
             // ---- higher bins to the row, the k-th bin into LDS in list order:
             // thread t takes entries [base + t*EPT, base + (t+1)*EPT), so a
             // scan of the per-thread candidate counts places them in order
+            // (with 16-byte loads the key indices are read together with the
+            // scores rather than after them: one round trip per step)
+            constexpr int EPT = VEC ? kMergeEptV : kMergeEpt;
             int cpos = 0;
             int step = 0;
-            for (int base = 0; base < n; base += kMergeThreads * kMergeEpt, ++step) {
-                const int e0 = base + tid * kMergeEpt;
-                float sc[kMergeEpt];
-                uint32_t u[kMergeEpt];
+            for (int base = 0; base < n; base += kMergeThreads * EPT, ++step) {
+                const int e0 = base + tid * EPT;
+                float sc[EPT];
+                uint32_t u[EPT];
+                int32_t id[VEC ? EPT : 1];
                 int nc = 0;
+                if constexpr (VEC) {
 #pragma unroll
-                for (int j = 0; j < kMergeEpt; ++j) {
-                    const bool valid = e0 + j < n;
-                    sc[j] = valid ? rs[e0 + j] : 0.f;
-                    u[j] = valid ? order_key(sc[j]) : 0u;
+                    for (int q = 0; q < EPT / 4; ++q) {
+                        const int e = e0 + 4 * q;
+                        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+                        int4 x = make_int4(0, 0, 0, 0);
+                        if (e < n) {
+                            v = *reinterpret_cast<const float4 *>(rs + e);
+                            x = *reinterpret_cast<const int4 *>(ri + e);
+                        }
+                        sc[4 * q] = v.x, sc[4 * q + 1] = v.y, sc[4 * q + 2] = v.z, sc[4 * q + 3] = v.w;
+                        id[4 * q] = x.x, id[4 * q + 1] = x.y, id[4 * q + 2] = x.z, id[4 * q + 3] = x.w;
+                    }
+#pragma unroll
+                    for (int j = 0; j < EPT; ++j) u[j] = e0 + j < n ? order_key(sc[j]) : 0u;
+                } else {
+#pragma unroll
+                    for (int j = 0; j < EPT; ++j) {
+                        const bool valid = e0 + j < n;
+                        sc[j] = valid ? rs[e0 + j] : 0.f;
+                        u[j] = valid ? order_key(sc[j]) : 0u;
+                    }
                 }
+                auto index_of = [&](int j) {
+                    if constexpr (VEC) return id[j];
+                    else return ri[e0 + j];
+                };
 #pragma unroll
-                for (int j = 0; j < kMergeEpt; ++j) {
+                for (int j = 0; j < EPT; ++j) {
                     const bool valid = e0 + j < n;
                     const uint32_t bin = u[j] >> 20;
                     if (valid && bin > bstar) {
                         const int p = atomicAdd(&sh.out, 1);
-                        if (p < n_above) put(p, u[j], ri[e0 + j], sc[j]);
+                        if (p < n_above) put(p, u[j], index_of(j), sc[j]);
                     }
                     nc += (valid && bin == bstar) ? 1 : 0;
                 }
@@ -233,10 +284,10 @@ merge_splits_kernel(const int32_t *__restrict__ pidx, const float *__restrict__ 
                 }
                 int pos = cpos + wbase + int(incl) - nc;
 #pragma unroll
-                for (int j = 0; j < kMergeEpt; ++j) {
+                for (int j = 0; j < EPT; ++j) {
                     if (e0 + j < n && (u[j] >> 20) == bstar) {
                         sh.cu[pos] = u[j];
-                        sh.ci[pos] = ri[e0 + j];
+                        sh.ci[pos] = index_of(j);
                         ++pos;
                     }
                 }
@@ -347,14 +398,21 @@ hipError_t launch_merge_splits(const Plan &p, const int32_t *part_idx, const flo
     if (rows <= 0 || p.n_splits <= 1) return hipSuccess;
     const int64_t cap = int64_t(num_cus) * 4;
     const int grid = int(rows < cap ? rows : cap);
-    if (p.merge_sorts)
-        hipLaunchKernelGGL(merge_splits_kernel<true>, dim3(grid), dim3(kMergeThreads), 0, s,
-                           part_idx, part_score, rows, p.n_splits, p.k, p.sort_pow2, out_idx,
-                           out_score);
-    else
-        hipLaunchKernelGGL(merge_splits_kernel<false>, dim3(grid), dim3(kMergeThreads), 0, s,
-                           part_idx, part_score, rows, p.n_splits, p.k, p.sort_pow2, out_idx,
-                           out_score);
+    // 16-byte loads when every row's lists start 16-byte aligned
+    const bool vec = p.k % 4 == 0 && (reinterpret_cast<uintptr_t>(part_idx) & 15) == 0 &&
+                     (reinterpret_cast<uintptr_t>(part_score) & 15) == 0;
+#define CSA_MERGE_LAUNCH(SORTED, VEC)                                                          \
+    hipLaunchKernelGGL((merge_splits_kernel<SORTED, VEC>), dim3(grid), dim3(kMergeThreads), 0, \
+                       s, part_idx, part_score, rows, p.n_splits, p.k, p.sort_pow2, out_idx,    \
+                       out_score)
+    if (p.merge_sorts) {
+        if (vec) CSA_MERGE_LAUNCH(true, true);
+        else CSA_MERGE_LAUNCH(true, false);
+    } else {
+        if (vec) CSA_MERGE_LAUNCH(false, true);
+        else CSA_MERGE_LAUNCH(false, false);
+    }
+#undef CSA_MERGE_LAUNCH
     return hipGetLastError();
 }
 
