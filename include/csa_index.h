@@ -107,7 +107,7 @@ typedef struct {
  *                range yields the exact top-k of its keys and a merge pass
  *                selects the top-k of the ranges' lists.  0 = automatic: 1
  *                while the query blocks fill the device, otherwise enough
- *                ranges of at least max(2k, 1024) keys to fill it (short query
+ *                ranges of at least max(9k/8, 1024) keys to fill it (short query
  *                blocks, decode steps).  n >= 1 asks for n ranges (at most one
  *                per 64 visible keys).  The partial lists take B*S*G*k*8
  *                bytes of workspace: an automatic G is lowered to keep them
