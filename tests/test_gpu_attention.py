@@ -270,10 +270,12 @@ def test_entry_splits_caller_workspace(csa):
 
 @pytest.mark.parametrize("G", [1, 3])
 def test_equal_weights_exact_mean(csa, G):
-    """scale = 0 makes every weight exactly 1 (bf16 of 2^0): with integer
-    values the weighted sum and the weight count are exact in fp32, so the
-    output is bf16(f32(sum v) * f32(1 / n)), bit for bit, with and without
-    entry ranges; lse = log(n)."""
+    """scale = 0 makes every weight exactly 1 (bf16 of 2^0): the output is
+    the mean of the selected value rows.  Checked against the oracle (the
+    exact mean, within one bf16 step) and, since with integer values the
+    sum and the weight count are exact in fp32, bit for bit against
+    bf16(f32(sum v) * f32(1 / n)), with and without entry ranges; lse =
+    log(n)."""
     aw = AttnWorkload("mean", B=2, S=96, T=300, H=64, D=128, n_sel=200, m=1)
     inp = make_attn_inputs(aw, seed=13, device="cuda")
     g = torch.Generator(device="cpu").manual_seed(13)
@@ -284,7 +286,18 @@ def test_equal_weights_exact_mean(csa, G):
     vf = v.float().cpu().numpy()
     got = out.float().cpu().numpy()
     got_lse = lse.cpu().numpy()
+    import oracle
+    from csa_synth import storage_numpy
     for b in range(aw.B):
+        # the oracle (fp64) at scale 0: the exact mean of the selected value
+        # rows; the kernel's output is that mean rounded to bf16 (through an
+        # fp32 product), so within one bf16 step of it
+        o, o_lse, _ = oracle.sparse_attention(storage_numpy(inp["q"][b]), storage_numpy(inp["k"][b]),
+                                              storage_numpy(v[b]), idx[b], 0.0)
+        assert np.all(np.abs(got[b] - o) <= 2.0 ** -8 * np.abs(o)), b
+        assert np.array_equal(np.isneginf(got_lse[b]), np.isneginf(o_lse))
+        fin = np.isfinite(o_lse)
+        np.testing.assert_allclose(got_lse[b][fin], o_lse[fin], rtol=1e-6)
         for t in range(aw.S):
             sel = idx[b, t][(idx[b, t] >= 0) & (idx[b, t] < aw.T)]
             n = len(sel)
