@@ -118,13 +118,15 @@ typedef struct {
  *                with out_score = NULL plans for that by itself); other bits
  *                must be 0.
  *   key_tile     Compressed keys staged in LDS per workgroup step (one
- *                barrier each); 0 = the default: for H = 64, D = 128 rows
- *                sorted by the scoring kernel (next_pow2(k) <= 2048, one
- *                key range) 128 (bf16) or 256 (fp8), else 64.  64 works
- *                everywhere; 32, 128, 192 and 256 (bf16) and 128 and 256
- *                (fp8) are built for such H = 64, D = 128 calls only and
- *                return CSA_ERR_UNSUPPORTED elsewhere.  Affects speed only,
- *                never the result.
+ *                barrier each); 0 = the default: 128 for bf16 with H = 64,
+ *                D = 128; 256 for fp8 with H = 64, D = 128 and rows sorted
+ *                by the scoring kernel (next_pow2(k) <= 2048, one key
+ *                range); else 64.  64 works everywhere.  With rows sorted
+ *                by the scoring kernel and H = 64, D = 128, also 32, 128,
+ *                192 and 256 (bf16) and 128 and 256 (fp8); otherwise also
+ *                128 for bf16 with H = 64, D = 128.  Other values return
+ *                CSA_ERR_UNSUPPORTED.  Affects speed only, never the
+ *                result.
  *   reserved2    Must be 0.
  */
 typedef struct {

@@ -1528,6 +1528,14 @@ template <int H, int D, bool FP8>
 static hipError_t launch_one(const StreamArgs &a, int grid, hipStream_t s)
 {
     if (a.sort_e == 0) {
+        if constexpr (H == 64 && D == 128 && !FP8) {
+            if (a.key_tile == 128) {
+                hipLaunchKernelGGL((stream_topk_kernel<H, D, FP8, true, 128>), dim3(grid),
+                                   dim3(kThreads), 0, s, a);
+                return hipGetLastError();
+            }
+        }
+        if (a.key_tile != kKeysPerTile) return hipErrorInvalidValue;
         hipLaunchKernelGGL((stream_topk_kernel<H, D, FP8, true>), dim3(grid), dim3(kThreads), 0,
                            s, a);
         return hipGetLastError();

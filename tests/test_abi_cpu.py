@@ -414,14 +414,15 @@ def test_static_entry_point_validation(lib):
 
 
 def test_key_tile_option(lib):
-    """Staged key tiles other than 64 exist for H = 64, D = 128 rows sorted
-    by the scoring kernel (bf16: 32 to 256; fp8: 128 and 256); elsewhere
-    they are unsupported."""
+    """Staged key tiles other than 64 exist for H = 64, D = 128: rows sorted
+    by the scoring kernel (bf16: 32 to 256; fp8: 128 and 256), and the
+    unsorted kernel (bf16: 128); elsewhere they are unsupported."""
     d = csa.make_desc(1, 65536, 16384, 64, 128)
     for kt in (32, 64, 128, 192, 256):
         assert csa.plan_query(d, 4, 2048, opts(key_tile=kt)).keys_per_tile == kt
     assert csa.plan_query(d, 4, 2048, opts()).keys_per_tile == 128   # default for this shape
-    assert csa.plan_query(d, 4, 4096, opts()).keys_per_tile == 64    # rows sorted separately
+    assert csa.plan_query(d, 4, 4096, opts()).keys_per_tile == 128   # rows sorted separately
+    assert csa.plan_query(d, 4, 4096, opts(key_tile=64)).keys_per_tile == 64
     assert csa.plan_query(csa.make_desc(1, 100, 25, 32, 128), 4, 8, opts()).keys_per_tile == 64
     f8 = csa.make_desc(1, 65536, 16384, 64, 128, B.CSA_FP8_E4M3FN, 16, 16)
     assert csa.plan_query(f8, 4, 2048, opts()).keys_per_tile == 256   # fp8 default
@@ -430,8 +431,10 @@ def test_key_tile_option(lib):
     assert bad(lib, f8, k=2048, opt=opts(key_tile=192)) == B.CSA_ERR_UNSUPPORTED
     assert bad(lib, f8, k=2048, opt=opts(key_tile=32)) == B.CSA_ERR_UNSUPPORTED
     assert bad(lib, d, k=2048, opt=opts(key_tile=96)) == B.CSA_ERR_UNSUPPORTED
-    assert bad(lib, d, k=4096, opt=opts(key_tile=128)) == B.CSA_ERR_UNSUPPORTED  # separate sort
-    assert bad(lib, d, k=2048, opt=opts(key_tile=128, key_splits=4)) == B.CSA_ERR_UNSUPPORTED
+    assert bad(lib, d, k=4096, opt=opts(key_tile=192)) == B.CSA_ERR_UNSUPPORTED  # separate sort
+    assert bad(lib, d, k=2048, opt=opts(key_tile=256, key_splits=4)) == B.CSA_ERR_UNSUPPORTED
+    assert csa.plan_query(d, 4, 2048, opts(key_splits=4)).keys_per_tile == 128
+    assert bad(lib, f8, k=4096, opt=opts(key_tile=128)) == B.CSA_ERR_UNSUPPORTED
     assert bad(lib, csa.make_desc(1, 100, 25, 32, 128), opt=opts(key_tile=128)) == \
         B.CSA_ERR_UNSUPPORTED
     assert bad(lib, d, opt=opts(key_tile=-64)) == B.CSA_ERR_INVALID_ARG

@@ -80,7 +80,8 @@ def test_dec64_gauss_all_rows(csa):
 
 def test_split_counts_bit_identical(csa):
     """1 (no split), a few uneven ranges, the automatic count, and ranges of
-    256 keys (smaller than k, so every range returns all its keys)."""
+    256 keys (smaller than k, so every range returns all its keys); and the
+    range kernel with 64-key and 128-key staged tiles."""
     wl = WORKLOADS["dec64"]
     inp = make_inputs(wl, seed=1, device="cuda")
     ref = None
@@ -92,6 +93,11 @@ def test_split_counts_bit_identical(csa):
             continue
         assert torch.equal(got[0], ref[0]), f"indices differ at key_splits={G}"
         assert torch.equal(got[1], ref[1]), f"scores differ at key_splits={G}"
+    # the range kernel's two staged key tiles (128 is its default here)
+    for G in (0, 7):
+        print(f"\n[case] {wl.name} key_splits={G} key_tile=64", flush=True)
+        got = _run(csa, inp, wl, key_splits=G, key_tile=64)
+        assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1]), G
 
 
 def test_dec32x4_batch(csa):
