@@ -13,7 +13,7 @@ namespace csa {
 
 constexpr int kMergeThreads = 512;
 constexpr int kMergeWaves = kMergeThreads / 64;
-constexpr int kMergeBins = 4096;  // top 12 bits of the order key
+constexpr int kMergeBins = 4096;  // 16-bit order-key prefixes in a window (see below)
 constexpr int kMergeCap = 6144;   // candidates of the k-th bin held in LDS
 constexpr int kMergeEpt = 8;      // consecutive list entries per thread in the gather
 // With 16-byte loads (k a multiple of 4, lists 16-byte aligned) each thread
@@ -32,6 +32,7 @@ struct MergeShared {
     uint32_t sel[2];
     int first;
     int out;
+    int anchor;
 };
 
 // Rank of this thread's flag among the flagged threads of the workgroup, in
@@ -97,11 +98,13 @@ __device__ __forceinline__ void digit_of_rank(const uint32_t *h, int need, uint3
 // ranges in ascending key order, so that equal scores appear in ascending
 // key order along the concatenated lists), and writes them to the output row
 // in no particular order.  One workgroup per position.  A histogram of the
-// top 12 bits of the order keys names the bin holding the k-th best; one
-// more pass writes every entry of a higher bin and gathers that bin's
-// entries, in list order, into LDS, where a radix select on the low 20 bits
-// finishes.  If the bin holds more than kMergeCap entries, an MSB-first
-// 4 x 8-bit radix select over the lists takes its place.  Equal keys are
+// 16-bit prefixes of the order keys (a window of kMergeBins prefixes around
+// the lists' leading entries) names the bin holding the k-th best; one more
+// pass writes every entry of a higher bin and gathers that bin's entries, in
+// list order, into LDS, where a radix select on the low 16 bits finishes.
+// If the bin holds more than kMergeCap entries or is an end bin of the
+// window (keys outside it are clamped there), an MSB-first 4 x 8-bit radix
+// select over the lists takes its place.  Equal keys are
 // taken in list order.  Padding entries (index -1, score -inf) order below
 // every finite score and fill the row when fewer than k keys are visible.
 // SORTED (rows of next_pow2(k) = pow2 <= kMaxFusedSort slots): the chosen
@@ -136,14 +139,31 @@ merge_splits_kernel(const int32_t *__restrict__ pidx, const float *__restrict__ 
             }
         };
 
-        // ---- histogram of the top 12 bits
+        // ---- histogram of 16-bit order-key prefixes (128 bins per binade of
+        // |score|) in a window of kMergeBins around an anchor: the largest
+        // prefix among the G lists' first entries.  Keys outside the window
+        // are clamped into its end bins (the bins stay in key order); a k-th
+        // best in an end bin takes the exact fallback below.  Bins this fine
+        // spread the LDS atomics, which on a window of whole binades pile
+        // onto a few counters.
 #pragma unroll
         for (int j = 0; j < PER; ++j) sh.hist[tid * PER + j] = 0u;
         if (tid == 0) {
             sh.first = kMergeThreads;
             sh.out = 0;
         }
+        if (wave == 0) {
+            int a = 0;
+            for (int r = lane; r < G; r += 64) a = max(a, int(order_key(rs[int64_t(r) * k]) >> 16));
+            a = wave_max(a);
+            if (lane == 0) sh.anchor = a;
+        }
         __syncthreads();
+        const int lo16 = sh.anchor - kMergeBins / 2;  // prefix of bin 0
+        auto bin_of = [&](uint32_t u) -> uint32_t {
+            const int b = int(u >> 16) - lo16;
+            return uint32_t(b < 0 ? 0 : (b > kMergeBins - 1 ? kMergeBins - 1 : b));
+        };
         constexpr int HB = VEC ? kMergeHistV : 4;  // entries per thread per step
         for (int base = 0; base < n; base += HB * kMergeThreads) {
             uint32_t bin[HB];
@@ -155,10 +175,10 @@ merge_splits_kernel(const int32_t *__restrict__ pidx, const float *__restrict__ 
                     const int e = base + tid * HB + 4 * q;
                     if (e < n) {
                         const float4 v = *reinterpret_cast<const float4 *>(rs + e);
-                        bin[4 * q] = order_key(v.x) >> 20;
-                        bin[4 * q + 1] = order_key(v.y) >> 20;
-                        bin[4 * q + 2] = order_key(v.z) >> 20;
-                        bin[4 * q + 3] = order_key(v.w) >> 20;
+                        bin[4 * q] = bin_of(order_key(v.x));
+                        bin[4 * q + 1] = bin_of(order_key(v.y));
+                        bin[4 * q + 2] = bin_of(order_key(v.z));
+                        bin[4 * q + 3] = bin_of(order_key(v.w));
                     } else {
                         bin[4 * q] = bin[4 * q + 1] = bin[4 * q + 2] = bin[4 * q + 3] =
                             uint32_t(kMergeBins);
@@ -168,7 +188,7 @@ merge_splits_kernel(const int32_t *__restrict__ pidx, const float *__restrict__ 
 #pragma unroll
                 for (int j = 0; j < HB; ++j) {
                     const int e = base + j * kMergeThreads + tid;
-                    bin[j] = e < n ? order_key(rs[e]) >> 20 : uint32_t(kMergeBins);
+                    bin[j] = e < n ? bin_of(order_key(rs[e])) : uint32_t(kMergeBins);
                 }
             }
 #pragma unroll
@@ -218,7 +238,8 @@ merge_splits_kernel(const int32_t *__restrict__ pidx, const float *__restrict__ 
 
         uint32_t prefix, pmask;
         int need = k - n_above;                  // still to take, >= 1
-        const bool fast = in_bin <= kMergeCap;
+        // (a clamped end bin holds keys of different prefixes)
+        const bool fast = in_bin <= kMergeCap && bstar > 0u && bstar < uint32_t(kMergeBins - 1);
         if (fast) {
             // ---- higher bins to the row, the k-th bin into LDS in list order:
             // thread t takes entries [base + t*EPT, base + (t+1)*EPT), so a
@@ -264,7 +285,7 @@ merge_splits_kernel(const int32_t *__restrict__ pidx, const float *__restrict__ 
 #pragma unroll
                 for (int j = 0; j < EPT; ++j) {
                     const bool valid = e0 + j < n;
-                    const uint32_t bin = u[j] >> 20;
+                    const uint32_t bin = bin_of(u[j]);
                     if (valid && bin > bstar) {
                         const int p = atomicAdd(&sh.out, 1);
                         if (p < n_above) put(p, u[j], index_of(j), sc[j]);
@@ -285,7 +306,7 @@ merge_splits_kernel(const int32_t *__restrict__ pidx, const float *__restrict__ 
                 int pos = cpos + wbase + int(incl) - nc;
 #pragma unroll
                 for (int j = 0; j < EPT; ++j) {
-                    if (e0 + j < n && (u[j] >> 20) == bstar) {
+                    if (e0 + j < n && bin_of(u[j]) == bstar) {
                         sh.cu[pos] = u[j];
                         sh.ci[pos] = index_of(j);
                         ++pos;
@@ -294,13 +315,14 @@ merge_splits_kernel(const int32_t *__restrict__ pidx, const float *__restrict__ 
                 cpos += tot;
             }
             __syncthreads();
-            // ---- radix select among the in_bin candidates: bits 19..12, 11..4, 3..0
-            prefix = bstar << 20;
-            pmask = 0xFFF00000u;
+            // ---- radix select among the in_bin candidates (one 16-bit
+            // prefix): bits 15..8, then 7..0
+            prefix = uint32_t(lo16 + int(bstar)) << 16;
+            pmask = 0xFFFF0000u;
             uint32_t *h = sh.hist;  // reused as a 256-bin histogram
-            for (int pass = 0; pass < 3; ++pass) {
-                const int shift = pass == 0 ? 12 : (pass == 1 ? 4 : 0);
-                const uint32_t dm = pass == 2 ? 0xFu : 0xFFu;
+            for (int pass = 0; pass < 2; ++pass) {
+                const int shift = pass == 0 ? 8 : 0;
+                const uint32_t dm = 0xFFu;
                 for (int i = tid; i < 256; i += kMergeThreads) h[i] = 0u;
                 __syncthreads();
                 for (int i = tid; i < in_bin; i += kMergeThreads) {
