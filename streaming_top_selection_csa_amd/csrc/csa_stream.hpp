@@ -101,10 +101,15 @@ __device__ __forceinline__ void lds_add(uint32_t *p, uint32_t v)
 }
 
 // Makes global stores of every lane of the wave visible to global loads of
-// the other lanes (write completion + L1 invalidation).
+// the other lanes: waits until this wave's stores are done, then a fence at
+// workgroup scope (all lanes run on one CU, whose vector L1 is written
+// through).  An agent-scope fence would also write back and invalidate the
+// XCD's whole L2 each time, evicting the key tiles that the other
+// workgroups of the XCD are streaming.
 __device__ __forceinline__ void wave_global_sync()
 {
-    __threadfence();
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
     __builtin_amdgcn_wave_barrier();
 }
 
