@@ -11,8 +11,11 @@ namespace csa {
 
 // ------------------------------------------------------------ key-range merge
 
-constexpr int kMergeThreads = 512;
-constexpr int kMergeWaves = kMergeThreads / 64;
+// Threads per row: 1,024 where rows are few and sorted here (short query
+// blocks: more loads in flight per step and more hands in the LDS sort),
+// 512 for the unsorted merge of many rows (measured faster there).
+template <bool SORTED> constexpr int kMergeThreads = SORTED ? 1024 : 512;
+constexpr int kMergeMaxWaves = 1024 / 64;
 constexpr int kMergeBins = 4096;  // 16-bit order-key prefixes in a window (see below)
 constexpr int kMergeCap = 6144;   // candidates of the k-th bin held in LDS
 constexpr int kMergeEpt = 8;      // consecutive list entries per thread in the gather
@@ -27,8 +30,8 @@ struct MergeShared {
     uint32_t hist[kMergeBins];
     uint32_t cu[kMergeCap];
     int32_t ci[kMergeCap];
-    uint32_t w[kMergeWaves];
-    uint32_t w2[2][kMergeWaves];
+    uint32_t w[kMergeMaxWaves];
+    uint32_t w2[2][kMergeMaxWaves];
     uint32_t sel[2];
     int first;
     int out;
@@ -37,6 +40,7 @@ struct MergeShared {
 
 // Rank of this thread's flag among the flagged threads of the workgroup, in
 // thread order, and their number (two barriers).
+template <int NW>
 __device__ __forceinline__ int block_rank(bool f, uint32_t *sw, int lane, int wave, int *total)
 {
     const uint64_t m = __ballot(f);
@@ -44,7 +48,7 @@ __device__ __forceinline__ int block_rank(bool f, uint32_t *sw, int lane, int wa
     __syncthreads();
     int base = 0, tot = 0;
 #pragma unroll
-    for (int v = 0; v < kMergeWaves; ++v) {
+    for (int v = 0; v < NW; ++v) {
         const int c = int(sw[v]);
         base += v < wave ? c : 0;
         tot += c;
@@ -112,7 +116,7 @@ __device__ __forceinline__ void digit_of_rank(const uint32_t *h, int need, uint3
 // index, and the row leaves sorted by (score desc, key index asc); out_score
 // may then be null.
 template <bool SORTED, bool VEC>
-__global__ void __launch_bounds__(kMergeThreads)
+__global__ void __launch_bounds__(kMergeThreads<SORTED>)
 merge_splits_kernel(const int32_t *__restrict__ pidx, const float *__restrict__ pscore,
                     int64_t rows, int G, int k, int pow2, int32_t *__restrict__ out_idx,
                     float *__restrict__ out_score)
@@ -123,7 +127,9 @@ merge_splits_kernel(const int32_t *__restrict__ pidx, const float *__restrict__ 
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = G * k;
-    constexpr int PER = kMergeBins / kMergeThreads;  // histogram bins per thread
+    constexpr int NT = kMergeThreads<SORTED>;
+    constexpr int NW = NT / 64;
+    constexpr int PER = kMergeBins / NT;  // histogram bins per thread
     for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
         const int32_t *ri = pidx + row * n;
         const float *rs = pscore + row * n;
@@ -149,7 +155,7 @@ merge_splits_kernel(const int32_t *__restrict__ pidx, const float *__restrict__ 
 #pragma unroll
         for (int j = 0; j < PER; ++j) sh.hist[tid * PER + j] = 0u;
         if (tid == 0) {
-            sh.first = kMergeThreads;
+            sh.first = NT;
             sh.out = 0;
         }
         if (wave == 0) {
@@ -165,7 +171,7 @@ merge_splits_kernel(const int32_t *__restrict__ pidx, const float *__restrict__ 
             return uint32_t(b < 0 ? 0 : (b > kMergeBins - 1 ? kMergeBins - 1 : b));
         };
         constexpr int HB = VEC ? kMergeHistV : 4;  // entries per thread per step
-        for (int base = 0; base < n; base += HB * kMergeThreads) {
+        for (int base = 0; base < n; base += HB * NT) {
             uint32_t bin[HB];
             if constexpr (VEC) {
                 // thread t reads entries [base + t*HB, base + (t+1)*HB); n is
@@ -187,7 +193,7 @@ merge_splits_kernel(const int32_t *__restrict__ pidx, const float *__restrict__ 
             } else {
 #pragma unroll
                 for (int j = 0; j < HB; ++j) {
-                    const int e = base + j * kMergeThreads + tid;
+                    const int e = base + j * NT + tid;
                     bin[j] = e < n ? bin_of(order_key(rs[e])) : uint32_t(kMergeBins);
                 }
             }
@@ -212,7 +218,7 @@ merge_splits_kernel(const int32_t *__restrict__ pidx, const float *__restrict__ 
         __syncthreads();
         uint32_t pre = pw;
 #pragma unroll
-        for (int v = 0; v < kMergeWaves; ++v) pre += v < wave ? sh.w[v] : 0u;
+        for (int v = 0; v < NW; ++v) pre += v < wave ? sh.w[v] : 0u;
         const uint64_t bal = __ballot(pre >= uint32_t(k));
         if (lane == 0 && bal)
             atomicMin(&sh.first, wave * 64 + __ffsll(static_cast<unsigned long long>(bal)) - 1);
@@ -249,7 +255,7 @@ merge_splits_kernel(const int32_t *__restrict__ pidx, const float *__restrict__ 
             constexpr int EPT = VEC ? kMergeEptV : kMergeEpt;
             int cpos = 0;
             int step = 0;
-            for (int base = 0; base < n; base += kMergeThreads * EPT, ++step) {
+            for (int base = 0; base < n; base += NT * EPT, ++step) {
                 const int e0 = base + tid * EPT;
                 float sc[EPT];
                 uint32_t u[EPT];
@@ -298,7 +304,7 @@ merge_splits_kernel(const int32_t *__restrict__ pidx, const float *__restrict__ 
                 __syncthreads();
                 int wbase = 0, tot = 0;
 #pragma unroll
-                for (int v = 0; v < kMergeWaves; ++v) {
+                for (int v = 0; v < NW; ++v) {
                     const int c2 = int(w2[v]);
                     wbase += v < wave ? c2 : 0;
                     tot += c2;
@@ -323,9 +329,9 @@ merge_splits_kernel(const int32_t *__restrict__ pidx, const float *__restrict__ 
             for (int pass = 0; pass < 2; ++pass) {
                 const int shift = pass == 0 ? 8 : 0;
                 const uint32_t dm = 0xFFu;
-                for (int i = tid; i < 256; i += kMergeThreads) h[i] = 0u;
+                for (int i = tid; i < 256; i += NT) h[i] = 0u;
                 __syncthreads();
-                for (int i = tid; i < in_bin; i += kMergeThreads) {
+                for (int i = tid; i < in_bin; i += NT) {
                     const uint32_t u = sh.cu[i];
                     if ((u & pmask) == prefix) atomicAdd(&h[(u >> shift) & dm], 1u);
                 }
@@ -339,7 +345,7 @@ merge_splits_kernel(const int32_t *__restrict__ pidx, const float *__restrict__ 
             // ---- larger keys of the bin, then the first `need` equal ones
             const int n_gt = k - need;
             int eq_base = 0;
-            for (int base = 0; base < in_bin; base += kMergeThreads) {
+            for (int base = 0; base < in_bin; base += NT) {
                 const int i = base + tid;
                 const uint32_t u = i < in_bin ? sh.cu[i] : 0u;
                 const bool gt = i < in_bin && u > prefix;
@@ -349,7 +355,7 @@ merge_splits_kernel(const int32_t *__restrict__ pidx, const float *__restrict__ 
                     if (p < n_gt) put(p, u, sh.ci[i], key_to_float(u));
                 }
                 int tot;
-                const int r = eq_base + block_rank(eq, sh.w, lane, wave, &tot);
+                const int r = eq_base + block_rank<NW>(eq, sh.w, lane, wave, &tot);
                 if (eq && r < need) put(n_gt + r, u, sh.ci[i], key_to_float(u));
                 eq_base += tot;
             }
@@ -360,9 +366,9 @@ merge_splits_kernel(const int32_t *__restrict__ pidx, const float *__restrict__ 
             need = k;
             uint32_t *h = sh.hist;
             for (int shift = 24; shift >= 0; shift -= 8) {
-                for (int i = tid; i < 256; i += kMergeThreads) h[i] = 0u;
+                for (int i = tid; i < 256; i += NT) h[i] = 0u;
                 __syncthreads();
-                for (int e = tid; e < n; e += kMergeThreads) {
+                for (int e = tid; e < n; e += NT) {
                     const uint32_t u = order_key(rs[e]);
                     if ((u & pmask) == prefix) atomicAdd(&h[(u >> shift) & 255u], 1u);
                 }
@@ -377,7 +383,7 @@ merge_splits_kernel(const int32_t *__restrict__ pidx, const float *__restrict__ 
             if (tid == 0) sh.out = 0;
             __syncthreads();
             int eq_base = 0;
-            for (int base = 0; base < n; base += kMergeThreads) {
+            for (int base = 0; base < n; base += NT) {
                 const int e = base + tid;
                 float sc = 0.f;
                 uint32_t u = 0u;
@@ -392,7 +398,7 @@ merge_splits_kernel(const int32_t *__restrict__ pidx, const float *__restrict__ 
                     if (p < n_gt) put(p, u, ri[e], sc);
                 }
                 int tot;
-                const int r = eq_base + block_rank(eq, sh.w, lane, wave, &tot);
+                const int r = eq_base + block_rank<NW>(eq, sh.w, lane, wave, &tot);
                 if (eq && r < need) put(n_gt + r, u, ri[e], sc);
                 eq_base += tot;
             }
@@ -400,10 +406,10 @@ merge_splits_kernel(const int32_t *__restrict__ pidx, const float *__restrict__ 
         __syncthreads();
         if constexpr (SORTED) {
             // the k chosen entries, padding slots after them, sorted in LDS
-            for (int e = k + tid; e < pow2; e += kMergeThreads) s_row[e] = ~0ull;
+            for (int e = k + tid; e < pow2; e += NT) s_row[e] = ~0ull;
             __syncthreads();
-            lds_bitonic_sort(s_row, pow2, tid, kMergeThreads);
-            for (int e = tid; e < k; e += kMergeThreads) {
+            lds_bitonic_sort(s_row, pow2, tid, NT);
+            for (int e = tid; e < k; e += NT) {
                 const unsigned long long key = s_row[e];
                 oi[e] = int32_t(uint32_t(key));
                 if (os) os[e] = key_to_float(~uint32_t(key >> 32));
@@ -424,7 +430,7 @@ hipError_t launch_merge_splits(const Plan &p, const int32_t *part_idx, const flo
     const bool vec = p.k % 4 == 0 && (reinterpret_cast<uintptr_t>(part_idx) & 15) == 0 &&
                      (reinterpret_cast<uintptr_t>(part_score) & 15) == 0;
 #define CSA_MERGE_LAUNCH(SORTED, VEC)                                                          \
-    hipLaunchKernelGGL((merge_splits_kernel<SORTED, VEC>), dim3(grid), dim3(kMergeThreads), 0, \
+    hipLaunchKernelGGL((merge_splits_kernel<SORTED, VEC>), dim3(grid), dim3(kMergeThreads<SORTED>), 0, \
                        s, part_idx, part_score, rows, p.n_splits, p.k, p.sort_pow2, out_idx,    \
                        out_score)
     if (p.merge_sorts) {
